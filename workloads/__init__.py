@@ -1,0 +1,264 @@
+"""Seeded synthetic inputs for paged attention (shared by the tests, the bench
+and the oracle's timing leg).
+
+This module draws random numbers and lays out plain arrays.  It holds none of
+the method's arithmetic: no slot or block-table computation, no attention,
+no fp8 encoding.  Block tables and slots are produced by a block manager
+(the oracle's or the library's own) from the ``free_order`` and lengths
+drawn here.
+
+Recipe (every draw from ``numpy.random.default_rng(seed)``, PCG64, in this
+order): sequence lengths -> pool permutation (the block manager's initial
+free list) -> K values -> V values -> Q values, all N(0, 1) float32, then a
+round-to-nearest-even cast to bf16 where the config is bf16 (torch's CPU
+cast).  K and V are drawn for every token of every sequence in the order
+the sequences are listed, tokens in logical order; fp8 configs pass K and V
+to the store as bf16 and quantise there with per-kv-head scales
+``amax(|x|) / 448`` taken over that head's bf16 values (fp32).
+
+The shapes follow one Qwen3-8B attention layer (32 query heads, 8 kv heads,
+head_dim 128); nothing here depends on model weights.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest even (torch cast)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass
+class PagedBatch:
+    """One step over a batch of sequences sharing one paged pool.
+
+    Sequence i already holds ``prior_lens[i]`` cached tokens and stores
+    ``new_lens[i]`` more during the step.  Decode sequences (``is_chunk``
+    False) store one token and ask one query; chunk sequences store a chunk
+    of ``new_lens[i]`` tokens whose rows are all queries.
+    """
+    name: str
+    seed: int
+    kv_dtype: str            # "f32" | "bf16" | "fp8"   (cache storage)
+    io_dtype: str            # "f32" | "bf16"           (q / out / new K,V)
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    free_order: np.ndarray   # int64 [num_blocks]
+    prior_lens: np.ndarray   # int64 [S]
+    new_lens: np.ndarray     # int64 [S]
+    is_chunk: np.ndarray     # bool  [S]
+    k: np.ndarray            # [sum(prior+new), Hkv, d]  io_dtype storage
+    v: np.ndarray
+    q_decode: np.ndarray     # [n_decode, Hq, d]          io_dtype storage
+    q_chunk: np.ndarray      # [sum new of chunk seqs, Hq, d]
+    k_scale: Optional[np.ndarray] = None   # float32 [Hkv] (fp8 only)
+    v_scale: Optional[np.ndarray] = None
+    scale: float = 0.0
+    partition_tokens: int = 512
+    notes: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.prior_lens)
+
+    @property
+    def tok_offsets(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.prior_lens + self.new_lens)]).astype(np.int64)
+
+    @property
+    def total_lens(self) -> np.ndarray:
+        return (self.prior_lens + self.new_lens).astype(np.int64)
+
+
+@dataclass
+class ForkBatch:
+    """A shared prompt forked into beams that then diverge token by token."""
+    name: str
+    seed: int
+    kv_dtype: str
+    io_dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    free_order: np.ndarray
+    shared_len: int          # tokens in the sequence at the moment of the fork
+    beams: int               # sequences after the fork (parent included)
+    steps: int               # divergent tokens appended per beam
+    k_shared: np.ndarray     # [shared_len, Hkv, d]
+    v_shared: np.ndarray
+    k_beam: np.ndarray       # [steps, beams, Hkv, d]
+    v_beam: np.ndarray
+    q: np.ndarray            # [beams, Hq, d]
+    k_scale: Optional[np.ndarray] = None
+    v_scale: Optional[np.ndarray] = None
+    scale: float = 0.0
+    partition_tokens: int = 512
+
+
+def _values(rng, shape, io_dtype):
+    x = rng.standard_normal(shape, dtype=np.float32)
+    return to_bf16_bits(x) if io_dtype == "bf16" else x
+
+
+def _pool_size(total_lens, block_size, factor=1.25):
+    need = int(sum(math.ceil(int(L) / block_size) for L in total_lens))
+    return max(1, int(math.ceil(factor * need)))
+
+
+def _head_scales(k_bits, v_bits):
+    """Per-kv-head fp32 scale amax/448 over that head's bf16 values."""
+    kf = np.abs(bf16_bits_to_f32(k_bits)).reshape(-1, k_bits.shape[-2], k_bits.shape[-1])
+    vf = np.abs(bf16_bits_to_f32(v_bits)).reshape(-1, v_bits.shape[-2], v_bits.shape[-1])
+    ks = (kf.max(axis=(0, 2)) / np.float32(E4M3_MAX)).astype(np.float32)
+    vs = (vf.max(axis=(0, 2)) / np.float32(E4M3_MAX)).astype(np.float32)
+    return ks, vs
+
+
+def paged_batch(name, seed, *, kv_dtype, io_dtype, Hq, Hkv, d, B, prior_lens, new_lens, is_chunk,
+                rng, pool=None, pool_factor=1.25, partition_tokens=512) -> PagedBatch:
+    prior_lens = np.asarray(prior_lens, dtype=np.int64)
+    new_lens = np.asarray(new_lens, dtype=np.int64)
+    is_chunk = np.asarray(is_chunk, dtype=bool)
+    total = prior_lens + new_lens
+    nb = pool if pool is not None else _pool_size(total, B, pool_factor)
+    free_order = rng.permutation(nb).astype(np.int64)
+    N = int(total.sum())
+    k = _values(rng, (N, Hkv, d), io_dtype)
+    v = _values(rng, (N, Hkv, d), io_dtype)
+    n_dec = int((~is_chunk).sum())
+    n_chunk_rows = int(new_lens[is_chunk].sum())
+    q_decode = _values(rng, (n_dec, Hq, d), io_dtype)
+    q_chunk = _values(rng, (n_chunk_rows, Hq, d), io_dtype)
+    ks = vs = None
+    if kv_dtype == "fp8":
+        ks, vs = _head_scales(k, v)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    return PagedBatch(name, seed, kv_dtype, io_dtype, Hq, Hkv, d, B, nb, free_order,
+                      prior_lens, new_lens, is_chunk, k, v, q_decode, q_chunk, ks, vs, scale,
+                      partition_tokens)
+
+
+# ----------------------------------------------------------------- configs
+def config1(small=False) -> PagedBatch:
+    """Tiny fp32 decode: lens {17,33,64,100}, Hq 4 / Hkv 2, d 64, B 16, pool 64."""
+    rng = np.random.default_rng(1)
+    lens = np.array([17, 33, 64, 100])
+    return paged_batch("tiny-fp32-decode", 1, kv_dtype="f32", io_dtype="f32", Hq=4, Hkv=2, d=64, B=16,
+                       prior_lens=lens - 1, new_lens=np.ones(4, np.int64), is_chunk=np.zeros(4, bool),
+                       rng=rng, pool=64)
+
+
+def config2(small=False) -> PagedBatch:
+    """Qwen3-8B decode layer: 32 seqs, L ~ U{512..4096}, bf16, B 16, pool 1.25x."""
+    seed = 2 if not small else 102
+    rng = np.random.default_rng(seed)
+    if small:
+        lens = rng.integers(1, 1400, size=6)
+    else:
+        lens = rng.integers(512, 4097, size=32)
+    return paged_batch("qwen3-8b-decode-32seq" if not small else "qwen3-8b-decode-small", seed,
+                       kv_dtype="bf16", io_dtype="bf16", Hq=32, Hkv=8, d=128, B=16,
+                       prior_lens=lens - 1, new_lens=np.ones(len(lens), np.int64),
+                       is_chunk=np.zeros(len(lens), bool), rng=rng)
+
+
+def config3(block_size=16, small=False) -> PagedBatch:
+    """Long-context decode: 128 seqs, L log-uniform [128, 32768], bf16, split-K 512.
+
+    The block-32 run reuses the lengths and the K/V/Q values of the block-16
+    run; only the pool (1.25x of the blocks needed at 32) and its permutation
+    are new (drawn from a second generator seeded 1003 / 1103).
+    """
+    seed = 3 if not small else 103
+    rng = np.random.default_rng(seed)
+    if small:
+        lens = np.round(np.exp(rng.uniform(np.log(1), np.log(3000), size=8))).astype(np.int64)
+    else:
+        lens = np.round(np.exp(rng.uniform(np.log(128), np.log(32768), size=128))).astype(np.int64)
+    base = paged_batch("long-context-decode-b16" if not small else "long-context-decode-small", seed,
+                       kv_dtype="bf16", io_dtype="bf16", Hq=32, Hkv=8, d=128, B=16,
+                       prior_lens=lens - 1, new_lens=np.ones(len(lens), np.int64),
+                       is_chunk=np.zeros(len(lens), bool), rng=rng)
+    if block_size == 16:
+        return base
+    rng2 = np.random.default_rng(seed + 1000)
+    nb = _pool_size(base.total_lens, block_size)
+    base.name = base.name.replace("b16", f"b{block_size}")
+    base.block_size = block_size
+    base.num_blocks = nb
+    base.free_order = rng2.permutation(nb).astype(np.int64)
+    return base
+
+
+def config4(small=False) -> PagedBatch:
+    """Mixed chunked-prefill batch: 8 chunks of 512 on prefixes U{0..7680} + 64 decodes U{256..4096}."""
+    seed = 4 if not small else 104
+    rng = np.random.default_rng(seed)
+    if small:
+        n_chunk, chunk, n_dec = 3, 80, 5
+        P = rng.integers(0, 601, size=n_chunk)
+        Ld = rng.integers(1, 700, size=n_dec)
+    else:
+        n_chunk, chunk, n_dec = 8, 512, 64
+        P = rng.integers(0, 7681, size=n_chunk)
+        Ld = rng.integers(256, 4097, size=n_dec)
+    prior = np.concatenate([P, Ld - 1])
+    new = np.concatenate([np.full(n_chunk, chunk), np.ones(n_dec, np.int64)])
+    is_chunk = np.concatenate([np.ones(n_chunk, bool), np.zeros(n_dec, bool)])
+    return paged_batch("mixed-chunked-prefill" if not small else "mixed-chunked-prefill-small", seed,
+                       kv_dtype="bf16", io_dtype="bf16", Hq=32, Hkv=8, d=128, B=16,
+                       prior_lens=prior, new_lens=new, is_chunk=is_chunk, rng=rng)
+
+
+def config5(small=False, literal_fork=False) -> ForkBatch:
+    """CoW fork with fp8 KV: a 2048-token prompt plus the parent's first generated
+    token (2049 shared tokens, so the tail block is partly filled and shared)
+    forked into 8 beams, 64 divergent tokens each.  ``literal_fork`` forks at
+    exactly 2048 tokens instead (a full tail block: no copy-on-write)."""
+    seed = 5 if not small else 105
+    rng = np.random.default_rng(seed)
+    if small:
+        prompt, beams, steps, Hq, Hkv, d = 48, 4, 21, 8, 2, 128
+    else:
+        prompt, beams, steps, Hq, Hkv, d = 2048, 8, 64, 32, 8, 128
+    shared = prompt if literal_fork else prompt + 1
+    B = 16
+    full_shared = shared // B          # blocks no beam ever writes again
+    blocks_needed = full_shared + beams * (math.ceil((shared + steps) / B) - full_shared)
+    nb = int(math.ceil(1.25 * blocks_needed))
+    free_order = rng.permutation(nb).astype(np.int64)
+    k_shared = _values(rng, (shared, Hkv, d), "bf16")
+    v_shared = _values(rng, (shared, Hkv, d), "bf16")
+    k_beam = _values(rng, (steps, beams, Hkv, d), "bf16")
+    v_beam = _values(rng, (steps, beams, Hkv, d), "bf16")
+    q = _values(rng, (beams, Hq, d), "bf16")
+    ks, vs = _head_scales(np.concatenate([k_shared.reshape(-1, Hkv, d), k_beam.reshape(-1, Hkv, d)]),
+                          np.concatenate([v_shared.reshape(-1, Hkv, d), v_beam.reshape(-1, Hkv, d)]))
+    name = "cow-fork-fp8" + ("-literal2048" if literal_fork else "") + ("-small" if small else "")
+    return ForkBatch(name, seed, "fp8", "bf16", Hq, Hkv, d, B, nb, free_order, shared, beams, steps,
+                     k_shared, v_shared, k_beam, v_beam, q, ks, vs,
+                     float(np.float32(1.0 / math.sqrt(d))))
+
+
+def chunk_tokens_of(batch: PagedBatch):
+    """Helpers for laying out step inputs: per-sequence slices into k / v."""
+    off = batch.tok_offsets
+    return [(int(off[i]), int(batch.prior_lens[i]), int(batch.new_lens[i])) for i in range(batch.num_seqs)]
