@@ -1,0 +1,221 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+A step is one pass of the path over one batch: pa_store_kv of the step's new
+tokens, then the attention call(s).  The default workload is one Qwen3-8B
+attention layer in decode: 32 sequences with contexts uniform in
+[512, 4096], 32 query / 8 KV heads, head_dim 128, bf16, block size 16.  To
+keep the 256 MB last-level cache from serving the KV, each step uses the
+next of ``--layers`` independent layer caches (as a model's decode step
+walks its layers), each laid out with the same sequence lengths.
+
+Printed: one JSON line with the step throughput (algorithmic KV GB/s of the
+decode reads), the decode kernel's roofline against 8 TB/s, secondary
+measurements, and the oracle's CPU throughput on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6
+
+
+def kv_bytes(lens, hkv, d, es):
+    return int(np.sum(lens)) * 2 * hkv * d * es
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=8, help="distinct layer caches cycled through")
+    ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = library default)")
+    ap.add_argument("--no-extras", action="store_true", help="skip the secondary measurements")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    return ap.parse_args()
+
+
+def timed_calls(fn, reps, warm=3):
+    """Median / p10 / p90 ms of fn() measured with events on the current stream."""
+    import torch
+    for _ in range(warm):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
+
+
+def extras(pa, runner, W, torch):
+    """Secondary measurements: long-context decode at block 16 and 32, the
+    mixed chunked-prefill batch, the fp8 fork decode, bulk store."""
+    out = {}
+    for B in (16, 32):
+        b = W.config3(B)
+        g = runner.prepare(b)
+        runner.store_step(g)
+        ws = pa.decode_workspace(len(g.dec["idx"]), b.num_q_heads, b.head_dim, g.dec["max_len"], 512)
+        med, p10, p90 = timed_calls(lambda: runner.decode_step(g, partition_tokens=512, workspace=ws), 20)
+        byt = kv_bytes(g.dec["host_lens"], b.num_kv_heads, b.head_dim, 2)
+        out[f"long_context_decode_b{B}"] = dict(GBps=round(byt / med / 1e6, 1), ms=round(med, 4),
+                                                p10_ms=round(p10, 4), p90_ms=round(p90, 4),
+                                                frac=round(byt / med / 1e6 / HBM_PEAK_GBS, 4),
+                                                kv_bytes=byt, tokens=int(np.sum(g.dec["host_lens"])))
+        if B == 16:
+            T = g.prior_slots.numel()
+            med, _, _ = timed_calls(lambda: runner.fill_prior(g), 5, warm=1)
+            moved = T * b.num_kv_heads * b.head_dim * 2 * (2 + 2) + 4 * T
+            out["bulk_store_b16"] = dict(GBps=round(moved / med / 1e6, 1), ms=round(med, 3), tokens=T,
+                                         frac=round(moved / med / 1e6 / HBM_PEAK_GBS, 4))
+        del g
+        torch.cuda.empty_cache()
+    b = W.config4()
+    g = runner.prepare(b)
+    med, _, _ = timed_calls(lambda: runner.store_step(g), 20)
+    T = g.step_slots.numel()
+    out["mixed_store"] = dict(GBps=round(T * b.num_kv_heads * b.head_dim * 8 / med / 1e6, 1), ms=round(med, 4))
+    runner.store_step(g)
+    ws = pa.decode_workspace(len(g.dec["idx"]), b.num_q_heads, b.head_dim, g.dec["max_len"], 512)
+    med, _, _ = timed_calls(lambda: runner.decode_step(g, workspace=ws), 20)
+    byt = kv_bytes(g.dec["host_lens"], b.num_kv_heads, b.head_dim, 2)
+    out["mixed_decode"] = dict(GBps=round(byt / med / 1e6, 1), ms=round(med, 4))
+    try:
+        med, _, _ = timed_calls(lambda: runner.chunk_step(g), 20)
+        fl = 0
+        for P, n in zip(g.chunk["host_prefix"], g.chunk["host_q"]):
+            fl += 4 * b.head_dim * b.num_q_heads * (int(n) * int(P) + int(n) * (int(n) + 1) // 2)
+        out["mixed_prefill_chunk"] = dict(TFLOPs=round(fl / med / 1e9, 1), ms=round(med, 4),
+                                          frac=round(fl / med / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4), flops=fl)
+    except Exception as e:  # the prefill kernel may be absent in a partial build
+        out["mixed_prefill_chunk"] = dict(error=str(e)[:200])
+    del g
+    fb = W.config5()
+    gf = runner.run_fork(fb)
+    med, _, _ = timed_calls(lambda: runner.fork_decode(gf), 20)
+    lens = [gf.bm.seq_len(x) for x in gf.beams]
+    byt = kv_bytes(lens, fb.num_kv_heads, fb.head_dim, 1)
+    out["fork_fp8_decode"] = dict(GBps_logical=round(byt / med / 1e6, 1), ms=round(med, 4),
+                                  note="cache resident: 8 beams share the prompt blocks")
+    return out
+
+
+def cpu_baseline(batch):
+    """The oracle (plain fp64 numpy) on a bounded sample of the workload:
+    the first sequences of the batch until about 10 s of work."""
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from oracle import paged
+    from tests import oracle_setup as OS
+    import threading
+    st = OS.build(batch)
+    dec = np.flatnonzero(~batch.is_chunk)
+    tables = OS.table_array([st.tables[i] for i in dec], st.pad_block)
+    lens = batch.total_lens[dec]
+    done, t0, byt = 0, time.perf_counter(), 0
+    while done < len(dec) and time.perf_counter() - t0 < 10.0:
+        s = done
+        paged.decode_attention(st.kc, st.vc, batch.kv_dtype, batch.q_decode[s:s + 1], batch.io_dtype,
+                               tables[s:s + 1], lens[s:s + 1], batch.scale)
+        byt += kv_bytes(lens[s:s + 1], batch.num_kv_heads, batch.head_dim, 2)
+        done += 1
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return dict(value=round(byt / dt / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
+                sample=f"fp64 numpy decode of {done} of {len(dec)} sequences ({int(np.sum(lens[:done]))} tokens) "
+                       f"in {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library runs on a single MI355X and has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as W
+    from paged_kv_attention_26_amd import binding as pa, runner
+
+    base = W.config2()
+    lens_all = base.total_lens
+    layers = []
+    for li in range(args.layers):
+        b = W.config2()
+        if li:
+            b.free_order = np.random.default_rng(1000 + li).permutation(b.num_blocks)
+        g = runner.prepare(b)
+        layers.append(g)
+    d0 = layers[0].dec
+    ws = pa.decode_workspace(len(d0["idx"]), base.num_q_heads, base.head_dim, d0["max_len"], args.partition)
+    out = torch.empty_like(d0["q"])
+    step_bytes = kv_bytes(lens_all, base.num_kv_heads, base.head_dim, 2)
+
+    def step(i):
+        g = layers[i % len(layers)]
+        runner.store_step(g)
+        return runner.decode_step(g, out=out, partition_tokens=args.partition, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        g = layers[i % len(layers)]
+        runner.store_step(g)
+        evs[i][0].record()
+        runner.decode_step(g, out=out, partition_tokens=args.partition, workspace=ws)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_avg = float(dec_ms.mean())
+    achieved = step_bytes / (dec_avg * 1e-3) / 1e9
+    rec = {
+        "metric": "paged decode KV GB/s (% HBM peak) + prefill-chunk TFLOP/s, Qwen3-8B layer",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3-8b decode layer: 32 seqs, ctx U[512,4096], Hq 32 / Hkv 8, d 128, "
+                               "bf16 KV, block 16, store 32 tokens + paged decode",
+                   "global_batch": int(len(lens_all)), "seq_len": int(np.max(lens_all)),
+                   "kv_tokens": int(np.sum(lens_all)), "layer_caches": args.layers,
+                   "partition_tokens": args.partition or 512, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa::decode_kernel<bf16, d128, B16, G4>",
+                     "kernel_ms_avg": round(dec_avg, 5), "kernel_ms_median": round(float(np.median(dec_ms)), 5),
+                     "algorithmic_bytes_per_launch": step_bytes},
+    }
+    if not args.no_extras:
+        del layers
+        torch.cuda.empty_cache()
+        rec["extras"] = extras(pa, runner, W, torch)
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(W.config2())
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

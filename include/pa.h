@@ -1,0 +1,219 @@
+/*
+ * pa.h -- C ABI of libpa: paged attention over a block-table-indexed KV cache
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (nanoPD page "自定义CUDA分页注意力内核" and "分页KV缓存"; serving-stack
+ * page section 2.2 "分页思想"): the KV cache is cut into fixed-size blocks of
+ * block_size tokens; each sequence keeps a block table mapping its logical
+ * block i to a physical block; every KV read goes through that table once.
+ * New tokens are written to their slots (physical_block * block_size +
+ * offset); forked sequences share blocks and copy a shared block before
+ * writing into it (copy on write); decode attends one query per sequence to
+ * all of its cached tokens; a prefill chunk attends causally to its paged
+ * prefix plus itself.
+ *
+ * Conventions for every call below
+ *  - All pointers are DEVICE pointers unless marked "host".  The caller owns
+ *    every buffer; the library never allocates or frees device memory.
+ *  - Calls are asynchronous on the given HIP stream (NULL = the default
+ *    stream).  Nothing is synchronised inside the library.
+ *  - Return value: 0 on success, or a negative PA_ERR_* code; the message of
+ *    the last failure on the calling thread is returned by pa_last_error().
+ *    Arguments are validated on the host before any HIP call, so a rejected
+ *    call launches nothing.
+ *  - Values inside device arrays (slots, block ids, lengths) are NOT checked:
+ *    a slot >= num_blocks * block_size, a block id >= num_blocks or a
+ *    context length above max_blocks_per_seq * block_size reads or writes out
+ *    of bounds (undefined behaviour), exactly like an out-of-range index.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  PA_FP8_E4M3 is the OCP 8-bit float E4M3FN (bias 7, max
+ * +-448, no infinities, NaN = 0x7F / 0xFF), the FP8 KV format of the
+ * PD-engineering page, section 6.2 (KV 缓存的精度压缩). */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
+
+enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL                         */
+  PA_ERR_SHAPE = -2,       /* inconsistent sizes (num_q_heads % num_kv_heads, ...)*/
+  PA_ERR_DTYPE = -3,       /* unsupported dtype combination                      */
+  PA_ERR_UNSUPPORTED = -4, /* head_dim / block_size / group size not compiled   */
+  PA_ERR_WORKSPACE = -5,   /* workspace smaller than pa_decode_workspace_bytes() */
+  PA_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed         */
+  PA_ERR_NO_BLOCKS = -7    /* block manager: the pool has no free block          */
+};
+
+/* A paged KV cache (the pools are device memory owned by the caller).
+ *
+ * Layout, per pool, row-major:
+ *   k_cache[num_blocks][num_kv_heads][block_size][head_dim]
+ *       -- one token's key row of one kv head is contiguous;
+ *   v_cache[num_blocks][num_kv_heads][head_dim][block_size]
+ *       -- V is stored transposed inside each block: one head-dim column of
+ *          a block's tokens is contiguous.
+ * Token t of a sequence lives in physical block table[t / block_size] at
+ * offset t % block_size.
+ *
+ * dtype: PA_F32, PA_BF16 or PA_FP8_E4M3.  For PA_FP8_E4M3 a stored code c of
+ * kv head h means c * k_scale[h] (keys) or c * v_scale[h] (values);
+ * k_scale / v_scale are device arrays of num_kv_heads fp32 and must be NULL
+ * for the other dtypes.
+ * Supported: head_dim in {64, 128}; block_size in {16, 32}. */
+typedef struct {
+  void* k_cache;
+  void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t head_dim;
+  int32_t dtype; /* pa_dtype */
+} pa_kv_cache;
+
+/* Store new K/V rows into their slots (nanoPD page, "paged KV store" of the
+ * paged_attention extension; serving-stack page section 2.3: a token goes to
+ * its sequence's last block at offset length % block_size).
+ *
+ *   k_new, v_new : [num_tokens][num_kv_heads][head_dim] of in_dtype, contiguous.
+ *   slot_mapping : [num_tokens] int32; slot = block * block_size + offset;
+ *                  a negative slot skips that token.
+ * For every token t with slot >= 0 and every kv head h:
+ *   k_cache[slot / bs][h][slot % bs][:] = enc(k_new[t][h][:])
+ *   v_cache[slot / bs][h][:][slot % bs] = enc(v_new[t][h][:])
+ * enc is the identity when in_dtype == cache dtype (F32->F32, BF16->BF16,
+ * bit-exact).  For an FP8 cache in_dtype must be BF16 and
+ * enc(x) = e4m3fn_round_nearest_even_saturate(float(x) / scale[h]) with an
+ * IEEE fp32 division; magnitudes above 448 saturate to +-448, NaN stays NaN.
+ * Two tokens with the same slot in one call: which one lands is unspecified.
+ * num_tokens == 0 is a no-op. */
+int pa_store_kv(const pa_kv_cache* cache, const void* k_new, const void* v_new, int32_t in_dtype,
+                const int32_t* slot_mapping, int32_t num_tokens, void* hip_stream);
+
+/* Copy whole blocks (copy on write for forked / beam sequences: nanoPD page
+ * "写时复制(Copy-on-Write)用于束搜索和投机解码的分支"; serving-stack page
+ * section 2.3, cow()).
+ *   src_dst : [num_pairs][2] int32 pairs (src, dst); for each pair
+ *             k_cache[dst] = k_cache[src] and v_cache[dst] = v_cache[src]
+ *             (all kv heads, the whole block, bit-exact).
+ * The dst ids must be distinct and must not appear as a src in the same
+ * call (then the copy order cannot matter).  num_pairs == 0 is a no-op. */
+int pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src_dst, int32_t num_pairs,
+                   void* hip_stream);
+
+/* Bytes of device workspace pa_decode needs for these sizes (host call, no
+ * HIP).  partition_tokens as for pa_decode (0 = the default, 512).  Returns
+ * 0 for invalid sizes. */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_tokens);
+
+/* Paged decode attention: one query token per sequence, grouped-query heads
+ * (PD-engineering page section 6.2: 8 KV heads shared by 32 query heads;
+ * query head h reads kv head h / (num_q_heads / num_kv_heads)).
+ *
+ *   q   : [num_seqs][num_q_heads][head_dim] of q_dtype
+ *   out : [num_seqs][num_q_heads][head_dim] of out_dtype
+ *   block_table  : [num_seqs][max_blocks_per_seq] int32 physical block ids;
+ *                  entries past a sequence's last block are never read.
+ *   context_lens : [num_seqs] int32, tokens to attend to, including the one
+ *                  just stored.  A length of 0 gives an output of 0.
+ *   max_context_len : host upper bound of context_lens (sizes the launch).
+ *   out[s][h] = sum_i softmax_i(scale * <q[s][h], k_i>) * v_i over tokens
+ *   i < context_lens[s], accumulated in fp32.
+ *
+ * Long contexts are split into partitions of partition_tokens tokens
+ * (0 = 512; otherwise a multiple of 64 and at most 64 * block_size); each
+ * partition keeps a running max / sum and the partitions are merged by
+ * log-sum-exp rescaling.  The result does not depend on partition_tokens
+ * beyond fp32 rounding.
+ *
+ * dtypes: F32 cache -> q, out F32; BF16 cache -> q, out BF16;
+ * FP8 cache -> q, out BF16.
+ *
+ * workspace: device memory of at least pa_decode_workspace_bytes() bytes.
+ * It must be zero-filled before its first use; every call leaves its
+ * counters zero again when it completes, so one workspace serves any number
+ * of successive calls on one stream.  Two calls that may run at the same
+ * time must not share a workspace. */
+int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
+              int32_t num_seqs, int32_t num_q_heads, float scale, const int32_t* block_table,
+              int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+              int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Chunked-prefill attention (nanoPD page "分块预填充"; PD-engineering page
+ * section 6.1; serving-stack page section 5.2): sequence j appends a chunk
+ * of q_len_j = cu_q_lens[j+1] - cu_q_lens[j] tokens, already stored in the
+ * cache by pa_store_kv, after P_j = seq_lens[j] - q_len_j cached tokens.
+ * Chunk row t (absolute position P_j + t) attends to tokens 0 .. P_j + t.
+ *
+ *   q   : [cu_q_lens[num_seqs]][num_q_heads][head_dim] BF16
+ *   out : same shape, BF16
+ *   cu_q_lens : [num_seqs + 1] int32, non-decreasing, cu_q_lens[0] == 0
+ *   seq_lens  : [num_seqs] int32, tokens of the sequence including the chunk
+ *   block_table : [num_seqs][max_blocks_per_seq] int32
+ *   max_q_len, max_seq_len : host upper bounds (size the launch)
+ * QK^T and PV run on bf16 matrix cores with fp32 accumulation; the
+ * probabilities are rounded to bf16 for PV.  Supported: BF16 cache,
+ * head_dim 128. */
+int pa_prefill_chunk(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* out,
+                     int32_t out_dtype, int32_t num_seqs, int32_t num_q_heads, float scale,
+                     const int32_t* cu_q_lens, const int32_t* seq_lens, const int32_t* block_table,
+                     int32_t max_blocks_per_seq, int32_t max_q_len, int32_t max_seq_len,
+                     void* hip_stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Host block manager (host memory only, no HIP): the paged allocator whose
+ * decisions the kernels above consume as data (serving-stack page section
+ * 2.3: allocate / incref / free / cow / append / fork / release).
+ *  - the free list starts as free_order (host, a permutation of
+ *    0..num_blocks-1; NULL = 0,1,2,...); allocation takes the LAST entry of
+ *    the list and freed blocks are appended to its end;
+ *  - appending to a sequence whose length is a multiple of block_size takes
+ *    a new block; otherwise a shared tail block (reference count > 1) is
+ *    first copied: a new block is taken, the pair (old, new) is queued for
+ *    pa_copy_blocks and the old block loses one reference.
+ * All ids are int32; functions returning int return PA_ERR_* on failure.
+ * Not thread-safe: one manager per thread. */
+typedef struct pa_block_manager pa_block_manager;
+
+pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order);
+void pa_bm_destroy(pa_block_manager* bm);
+/* New empty sequence; returns its id (>= 0). */
+int32_t pa_bm_seq_new(pa_block_manager* bm);
+/* Append n tokens to seq, writing their slots to slots_out (host, [n]).
+ * Returns the number appended: n, or fewer when the pool ran out (then
+ * pa_last_error() says so and the sequence keeps the tokens appended). */
+int32_t pa_bm_append(pa_block_manager* bm, int32_t seq, int32_t n, int32_t* slots_out);
+/* Fork: a new sequence sharing every block of seq; returns its id. */
+int32_t pa_bm_fork(pa_block_manager* bm, int32_t seq);
+/* Drop every block reference of seq; the id stays valid and empty. */
+int pa_bm_release(pa_block_manager* bm, int32_t seq);
+/* Move up to max_pairs queued (src, dst) copy pairs to pairs_out (host,
+ * [max_pairs][2]); returns how many were moved (oldest first). */
+int32_t pa_bm_take_copies(pa_block_manager* bm, int32_t* pairs_out, int32_t max_pairs);
+int32_t pa_bm_seq_len(const pa_block_manager* bm, int32_t seq);
+/* Copy seq's block table to table_out (host, [max_entries]); returns the
+ * number of blocks it holds (which may exceed max_entries). */
+int32_t pa_bm_block_table(const pa_block_manager* bm, int32_t seq, int32_t* table_out,
+                          int32_t max_entries);
+int32_t pa_bm_used_blocks(const pa_block_manager* bm);
+int32_t pa_bm_ref_count(const pa_block_manager* bm, int32_t block);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

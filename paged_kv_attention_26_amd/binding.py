@@ -1,0 +1,248 @@
+"""Python binding of libpa: torch tensors in, C ABI calls out.
+
+Marshalling only: shape / dtype / device checks, pointers, the current HIP
+stream.  All computation happens in libpa's kernels.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+DTYPE_CODES = {"f32": L.PA_F32, "bf16": L.PA_BF16, "fp8": L.PA_FP8_E4M3}
+CACHE_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+IO_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.bfloat16}
+# NaN patterns written into fresh pools so that a stray read shows up as NaN
+POISON = {"f32": (torch.int32, 0x7FC00000), "bf16": (torch.int16, 0x7FC0), "fp8": (torch.uint8, 0x7F)}
+
+
+def _stream(stream) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> C.c_void_p:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return C.c_void_p(t.data_ptr())
+
+
+class KVCache:
+    """A paged KV cache: K pool [NB, Hkv, B, D] and transposed V pool [NB, Hkv, D, B]."""
+
+    def __init__(self, k_cache: torch.Tensor, v_cache: torch.Tensor, dtype: str,
+                 k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None):
+        if dtype not in DTYPE_CODES:
+            raise ValueError(f"unknown cache dtype {dtype}")
+        nb, hkv, bs, d = k_cache.shape
+        if tuple(v_cache.shape) != (nb, hkv, d, bs):
+            raise ValueError(f"v_cache must be [NB, Hkv, D, B] = {(nb, hkv, d, bs)}, got {tuple(v_cache.shape)}")
+        _dev(k_cache, "k_cache", CACHE_TORCH[dtype])
+        _dev(v_cache, "v_cache", CACHE_TORCH[dtype])
+        if dtype == "fp8":
+            _dev(k_scale, "k_scale", torch.float32)
+            _dev(v_scale, "v_scale", torch.float32)
+        self.k_cache, self.v_cache, self.dtype = k_cache, v_cache, dtype
+        self.k_scale, self.v_scale = k_scale, v_scale
+        self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim = nb, hkv, bs, d
+        self.desc = L.PaKvCache(k_cache.data_ptr(), v_cache.data_ptr(),
+                                k_scale.data_ptr() if k_scale is not None else None,
+                                v_scale.data_ptr() if v_scale is not None else None,
+                                nb, hkv, bs, d, DTYPE_CODES[dtype])
+
+    @property
+    def io_dtype(self) -> torch.dtype:
+        return IO_TORCH[self.dtype]
+
+
+def alloc_cache(num_blocks, num_kv_heads, block_size, head_dim, dtype, device="cuda",
+                k_scale=None, v_scale=None, poison=True) -> KVCache:
+    tdt = CACHE_TORCH[dtype]
+    k = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=tdt, device=device)
+    v = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=tdt, device=device)
+    if poison:
+        view_dt, bits = POISON[dtype]
+        k.view(view_dt).fill_(bits)
+        v.view(view_dt).fill_(bits)
+    if dtype == "fp8":
+        k_scale = torch.as_tensor(k_scale, dtype=torch.float32).to(device).contiguous()
+        v_scale = torch.as_tensor(v_scale, dtype=torch.float32).to(device).contiguous()
+    return KVCache(k, v, dtype, k_scale, v_scale)
+
+
+def store_kv(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+             stream=None) -> None:
+    T = slot_mapping.numel()
+    shape = (T, cache.num_kv_heads, cache.head_dim)
+    if tuple(k_new.shape) != shape or tuple(v_new.shape) != shape:
+        raise ValueError(f"k_new / v_new must be {shape}")
+    io = DTYPE_CODES["f32"] if cache.dtype == "f32" else DTYPE_CODES["bf16"]
+    L.check(L.lib().pa_store_kv(C.byref(cache.desc), _dev(k_new, "k_new", cache.io_dtype),
+                                _dev(v_new, "v_new", cache.io_dtype), io,
+                                _dev(slot_mapping, "slot_mapping", torch.int32), T, _stream(stream)),
+            "pa_store_kv")
+
+
+def copy_blocks(cache: KVCache, pairs: torch.Tensor, stream=None) -> None:
+    n = pairs.shape[0] if pairs.numel() else 0
+    if n and tuple(pairs.shape) != (n, 2):
+        raise ValueError("pairs must be [n, 2]")
+    ptr = _dev(pairs, "pairs", torch.int32) if n else None
+    L.check(L.lib().pa_copy_blocks(C.byref(cache.desc), ptr, n, _stream(stream)), "pa_copy_blocks")
+
+
+def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens=0) -> int:
+    return int(L.lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                                 partition_tokens))
+
+
+def decode_workspace(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens=0,
+                     device="cuda") -> torch.Tensor:
+    """Zero-filled workspace (pa_decode leaves it zeroed again after each call)."""
+    n = decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def decode(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor, context_lens: torch.Tensor,
+           max_context_len: int, scale: float, out: Optional[torch.Tensor] = None, partition_tokens: int = 0,
+           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    S, Hq, D = q.shape
+    if D != cache.head_dim:
+        raise ValueError("q head_dim does not match the cache")
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = decode_workspace(S, Hq, D, max_context_len, partition_tokens, device=q.device)
+    if block_table.dim() != 2 or block_table.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_table must be [S, max_blocks] and context_lens [S]")
+    io = DTYPE_CODES["f32"] if cache.dtype == "f32" else DTYPE_CODES["bf16"]
+    L.check(L.lib().pa_decode(C.byref(cache.desc), _dev(q, "q", cache.io_dtype), io,
+                              _dev(out, "out", cache.io_dtype), io, S, Hq, float(scale),
+                              _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+                              _dev(context_lens, "context_lens", torch.int32), int(max_context_len),
+                              int(partition_tokens), _dev(workspace, "workspace"), workspace.numel(),
+                              _stream(stream)),
+            "pa_decode")
+    return out
+
+
+def prefill_chunk(cache: KVCache, q: torch.Tensor, cu_q_lens: torch.Tensor, seq_lens: torch.Tensor,
+                  block_table: torch.Tensor, max_q_len: int, max_seq_len: int, scale: float,
+                  out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    T, Hq, D = q.shape
+    S = seq_lens.numel()
+    if out is None:
+        out = torch.empty_like(q)
+    if cu_q_lens.numel() != S + 1 or block_table.dim() != 2 or block_table.shape[0] != S:
+        raise ValueError("cu_q_lens must be [S+1] and block_table [S, max_blocks]")
+    L.check(L.lib().pa_prefill_chunk(C.byref(cache.desc), _dev(q, "q", torch.bfloat16), DTYPE_CODES["bf16"],
+                                     _dev(out, "out", torch.bfloat16), DTYPE_CODES["bf16"], S, Hq, float(scale),
+                                     _dev(cu_q_lens, "cu_q_lens", torch.int32),
+                                     _dev(seq_lens, "seq_lens", torch.int32),
+                                     _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+                                     int(max_q_len), int(max_seq_len), _stream(stream)),
+            "pa_prefill_chunk")
+    return out
+
+
+class BlockManager:
+    """Host block manager of libpa (pa_bm_*): allocate / fork / copy on write."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        self._l = L.lib()
+        fo = None
+        if free_order is not None:
+            self._fo = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+            fo = self._fo.ctypes.data_as(C.POINTER(C.c_int32))
+        self._h = self._l.pa_bm_create(int(num_blocks), int(block_size), fo)
+        if not self._h:
+            raise L.PaError(L.PA_ERR_SHAPE, "pa_bm_create")
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._l.pa_bm_destroy(h)
+            self._h = None
+
+    def seq_new(self) -> int:
+        s = self._l.pa_bm_seq_new(self._h)
+        if s < 0:
+            raise L.PaError(s, "pa_bm_seq_new")
+        return s
+
+    def append(self, seq: int, n: int) -> np.ndarray:
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        got = self._l.pa_bm_append(self._h, seq, n, out.ctypes.data_as(C.POINTER(C.c_int32)))
+        if got < 0:
+            raise L.PaError(got, "pa_bm_append")
+        if got < n:
+            raise MemoryError(self._l.pa_last_error().decode())
+        return out[:n]
+
+    def fork(self, seq: int) -> int:
+        s = self._l.pa_bm_fork(self._h, seq)
+        if s < 0:
+            raise L.PaError(s, "pa_bm_fork")
+        return s
+
+    def release(self, seq: int) -> None:
+        L.check(self._l.pa_bm_release(self._h, seq), "pa_bm_release")
+
+    def take_copies(self) -> np.ndarray:
+        pairs = []
+        buf = np.zeros((64, 2), dtype=np.int32)
+        while True:
+            n = self._l.pa_bm_take_copies(self._h, buf.ctypes.data_as(C.POINTER(C.c_int32)), 64)
+            if n < 0:
+                raise L.PaError(n, "pa_bm_take_copies")
+            pairs.append(buf[:n].copy())
+            if n < 64:
+                break
+        return np.concatenate(pairs).reshape(-1, 2)
+
+    def seq_len(self, seq: int) -> int:
+        return int(self._l.pa_bm_seq_len(self._h, seq))
+
+    def block_table(self, seq: int) -> list:
+        n = self._l.pa_bm_block_table(self._h, seq, None, 0)
+        if n < 0:
+            raise L.PaError(n, "pa_bm_block_table")
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        self._l.pa_bm_block_table(self._h, seq, out.ctypes.data_as(C.POINTER(C.c_int32)), n)
+        return out[:n].tolist()
+
+    def block_tables(self, seqs, pad: int, min_width: int = 1) -> np.ndarray:
+        rows = [self.block_table(s) for s in seqs]
+        width = max([min_width] + [len(r) for r in rows])
+        out = np.full((len(rows), width), pad, dtype=np.int32)
+        for i, r in enumerate(rows):
+            out[i, :len(r)] = r
+        return out
+
+    @property
+    def used_blocks(self) -> int:
+        return int(self._l.pa_bm_used_blocks(self._h))
+
+    def ref_count(self, block: int) -> int:
+        r = self._l.pa_bm_ref_count(self._h, block)
+        if r < 0:
+            raise L.PaError(r, "pa_bm_ref_count")
+        return int(r)
+
+    def unused_block(self) -> int:
+        for b in range(self.num_blocks):
+            if self._l.pa_bm_ref_count(self._h, b) == 0:
+                return b
+        return 0

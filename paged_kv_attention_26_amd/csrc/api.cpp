@@ -1,0 +1,244 @@
+// libpa C ABI: argument validation, dtype/shape dispatch and launches.
+// Every check runs on the host before the first HIP call, so a rejected
+// call launches nothing and touches no device state.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace pa {
+hipError_t launch_decode_f32(const DecodeArgs&, int, int, int, int64_t, hipStream_t);
+hipError_t launch_decode_bf16(const DecodeArgs&, int, int, int, int64_t, hipStream_t);
+hipError_t launch_decode_fp8(const DecodeArgs&, int, int, int, int64_t, hipStream_t);
+}  // namespace pa
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+template <typename... A>
+int fail(int code, const char* fmt, A... args) {
+  snprintf(g_err, sizeof(g_err), fmt, args...);
+  return code;
+}
+int fail(int code, const char* msg) {
+  snprintf(g_err, sizeof(g_err), "%s", msg);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kDefaultPartition = 512;
+constexpr int kMaxSeqs = 8192;  // the decode kernel keeps a prefix over sequences in LDS
+
+int elem_bytes(int dt) { return dt == PA_F32 ? 4 : dt == PA_BF16 ? 2 : 1; }
+
+int check_cache(const pa_kv_cache* c) {
+  if (!c) return fail(PA_ERR_NULL, "cache descriptor is NULL");
+  if (!c->k_cache || !c->v_cache) return fail(PA_ERR_NULL, "k_cache / v_cache is NULL");
+  if (c->dtype != PA_F32 && c->dtype != PA_BF16 && c->dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_DTYPE, "unknown cache dtype %d", c->dtype);
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return fail(PA_ERR_SHAPE, "num_blocks / num_kv_heads must be > 0");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", c->head_dim);
+  if (c->block_size != 16 && c->block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (16 or 32)", c->block_size);
+  if (c->dtype == PA_FP8_E4M3) {
+    if (!c->k_scale || !c->v_scale) return fail(PA_ERR_NULL, "fp8 cache needs k_scale and v_scale");
+  } else if (c->k_scale || c->v_scale) {
+    return fail(PA_ERR_DTYPE, "k_scale / v_scale are only for an fp8 cache");
+  }
+  return PA_OK;
+}
+
+int io_dtype_for(int cache_dtype) { return cache_dtype == PA_F32 ? PA_F32 : PA_BF16; }
+
+int resolve_partition(int32_t p, int32_t block_size, int32_t* out) {
+  if (p == 0) p = kDefaultPartition;
+  if (p < 64 || p % 64 != 0) return fail(PA_ERR_SHAPE, "partition_tokens %d must be a positive multiple of 64", p);
+  if (p % block_size != 0 || p > 64 * block_size)
+    return fail(PA_ERR_SHAPE, "partition_tokens %d must be a multiple of block_size %d and at most %d", p,
+                block_size, 64 * block_size);
+  *out = p;
+  return PA_OK;
+}
+
+size_t workspace_bytes(int64_t S, int64_t Hq, int64_t D, int64_t max_ctx, int64_t P) {
+  const int64_t max_parts = max_ctx > 0 ? (max_ctx + P - 1) / P : 1;
+  return pa::decode_workspace_layout(S, Hq, D, max_parts).total;
+}
+
+}  // namespace
+
+namespace pa {
+
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+DecodeWorkspace decode_workspace_layout(int64_t S, int64_t Hq, int64_t D, int64_t max_parts) {
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  DecodeWorkspace w;
+  w.counters_off = 0;
+  w.ml_off = up(size_t(2 + S * Hq) * sizeof(int32_t));
+  w.acc_off = w.ml_off + up(size_t(S * Hq * max_parts * 2) * sizeof(float));
+  w.total = w.acc_off + up(size_t(S * Hq * max_parts * D) * sizeof(float));
+  return w;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int kv, int D, int B, int G, int64_t upper, hipStream_t s) {
+  switch (kv) {
+    case KV_F32: return launch_decode_f32(a, D, B, G, upper, s);
+    case KV_BF16: return launch_decode_bf16(a, D, B, G, upper, s);
+    default: return launch_decode_fp8(a, D, B, G, upper, s);
+  }
+}
+
+}  // namespace pa
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_err; }
+
+int pa_store_kv(const pa_kv_cache* cache, const void* k_new, const void* v_new, int32_t in_dtype,
+                const int32_t* slot_mapping, int32_t num_tokens, void* hip_stream) {
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens %d < 0", num_tokens);
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping) return fail(PA_ERR_NULL, "k_new / v_new / slot_mapping is NULL");
+  if (in_dtype != io_dtype_for(cache->dtype))
+    return fail(PA_ERR_DTYPE, "store into a %s cache takes %s input",
+                cache->dtype == PA_F32 ? "f32" : cache->dtype == PA_BF16 ? "bf16" : "fp8",
+                cache->dtype == PA_F32 ? "f32" : "bf16");
+  pa::StoreArgs a{cache->k_cache, cache->v_cache, cache->k_scale, cache->v_scale, k_new, v_new, slot_mapping,
+                  num_tokens, cache->num_kv_heads, cache->block_size, cache->head_dim};
+  const int kv = cache->dtype == PA_F32 ? pa::KV_F32 : cache->dtype == PA_BF16 ? pa::KV_BF16 : pa::KV_FP8;
+  hipError_t e = pa::launch_store_kv(a, kv, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_store_kv launch");
+  g_err[0] = 0;
+  return PA_OK;
+}
+
+int pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src_dst, int32_t num_pairs, void* hip_stream) {
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  if (num_pairs < 0) return fail(PA_ERR_SHAPE, "num_pairs %d < 0", num_pairs);
+  if (num_pairs == 0) return PA_OK;
+  if (!src_dst) return fail(PA_ERR_NULL, "src_dst is NULL");
+  pa::CopyArgs a{cache->k_cache, cache->v_cache, src_dst,
+                 size_t(cache->num_kv_heads) * cache->block_size * cache->head_dim * elem_bytes(cache->dtype)};
+  hipError_t e = pa::launch_copy_blocks(a, num_pairs, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_copy_blocks launch");
+  g_err[0] = 0;
+  return PA_OK;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_tokens) {
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  int32_t P = partition_tokens == 0 ? kDefaultPartition : partition_tokens;
+  if (P < 64 || P % 64) return 0;
+  return workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, P);
+}
+
+int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
+              int32_t num_seqs, int32_t num_q_heads, float scale, const int32_t* block_table,
+              int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+              int32_t partition_tokens, void* workspace, size_t workspace_bytes_given, void* hip_stream) {
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  if (num_seqs < 0 || num_seqs > kMaxSeqs) return fail(PA_ERR_SHAPE, "num_seqs %d outside 0..%d", num_seqs, kMaxSeqs);
+  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads)
+    return fail(PA_ERR_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                cache->num_kv_heads);
+  const int G = num_q_heads / cache->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(PA_ERR_UNSUPPORTED, "query group %d not in {1,2,4,8}", G);
+  const int io = io_dtype_for(cache->dtype);
+  if (q_dtype != io || out_dtype != io)
+    return fail(PA_ERR_DTYPE, "decode over this cache takes %s q and out", io == PA_F32 ? "f32" : "bf16");
+  if (max_context_len < 0) return fail(PA_ERR_SHAPE, "max_context_len %d < 0", max_context_len);
+  const int64_t need_blocks = (int64_t(max_context_len) + cache->block_size - 1) / cache->block_size;
+  if (max_blocks_per_seq < need_blocks || max_blocks_per_seq <= 0)
+    return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d < %lld blocks of max_context_len", max_blocks_per_seq,
+                (long long)need_blocks);
+  if (!(std::isfinite(scale))) return fail(PA_ERR_SHAPE, "scale is not finite");
+  int32_t P = 0;
+  rc = resolve_partition(partition_tokens, cache->block_size, &P);
+  if (rc) return rc;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !out || !block_table || !context_lens || !workspace)
+    return fail(PA_ERR_NULL, "q / out / block_table / context_lens / workspace is NULL");
+  const int64_t max_parts = max_context_len > 0 ? (int64_t(max_context_len) + P - 1) / P : 1;
+  const pa::DecodeWorkspace lay = pa::decode_workspace_layout(num_seqs, num_q_heads, cache->head_dim, max_parts);
+  if (workspace_bytes_given < lay.total)
+    return fail(PA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes_given, lay.total);
+  char* ws = static_cast<char*>(workspace);
+  pa::DecodeArgs a{};
+  a.k_cache = cache->k_cache;
+  a.v_cache = cache->v_cache;
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.q = q;
+  a.out = out;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.counters = reinterpret_cast<int32_t*>(ws + lay.counters_off);
+  a.part_ml = reinterpret_cast<float*>(ws + lay.ml_off);
+  a.part_acc = reinterpret_cast<float*>(ws + lay.acc_off);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.part_tokens = P;
+  a.max_parts = int32_t(max_parts);
+  const int kv = cache->dtype == PA_F32 ? pa::KV_F32 : cache->dtype == PA_BF16 ? pa::KV_BF16 : pa::KV_FP8;
+  const int64_t upper_items = int64_t(num_seqs) * cache->num_kv_heads * max_parts;
+  hipError_t e = pa::launch_decode(a, kv, cache->head_dim, cache->block_size, G, upper_items,
+                                   static_cast<hipStream_t>(hip_stream));
+  if (e == hipErrorInvalidValue) return fail(PA_ERR_UNSUPPORTED, "no decode kernel for this shape");
+  if (e != hipSuccess) return hip_fail(e, "pa_decode launch");
+  g_err[0] = 0;
+  return PA_OK;
+}
+
+int pa_prefill_chunk(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
+                     int32_t num_seqs, int32_t num_q_heads, float scale, const int32_t* cu_q_lens,
+                     const int32_t* seq_lens, const int32_t* block_table, int32_t max_blocks_per_seq,
+                     int32_t max_q_len, int32_t max_seq_len, void* hip_stream) {
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
+  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads)
+    return fail(PA_ERR_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                cache->num_kv_heads);
+  const int G = num_q_heads / cache->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(PA_ERR_UNSUPPORTED, "query group %d not in {1,2,4,8}", G);
+  if (cache->dtype != PA_BF16) return fail(PA_ERR_DTYPE, "pa_prefill_chunk needs a bf16 cache");
+  if (q_dtype != PA_BF16 || out_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "pa_prefill_chunk takes bf16 q and out");
+  if (cache->head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk supports head_dim 128");
+  if (max_q_len < 0 || max_seq_len < max_q_len)
+    return fail(PA_ERR_SHAPE, "need 0 <= max_q_len (%d) <= max_seq_len (%d)", max_q_len, max_seq_len);
+  const int64_t need_blocks = (int64_t(max_seq_len) + cache->block_size - 1) / cache->block_size;
+  if (max_blocks_per_seq < need_blocks || max_blocks_per_seq <= 0)
+    return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d < %lld blocks of max_seq_len", max_blocks_per_seq,
+                (long long)need_blocks);
+  if (!(std::isfinite(scale))) return fail(PA_ERR_SHAPE, "scale is not finite");
+  if (num_seqs == 0 || max_q_len == 0) return PA_OK;
+  if (!q || !out || !cu_q_lens || !seq_lens || !block_table)
+    return fail(PA_ERR_NULL, "q / out / cu_q_lens / seq_lens / block_table is NULL");
+  (void)hip_stream;
+  return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk kernel is not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Launch arguments and launcher entry points shared between libpa's C ABI
+// layer (api.cpp) and its kernels.  Host-visible plain structs only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Cache element kinds the kernels are compiled for.
+enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+
+struct StoreArgs {
+  void* k_cache;
+  void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slot_mapping;
+  int32_t num_tokens, num_kv_heads, block_size, head_dim;
+};
+
+struct CopyArgs {
+  void* k_cache;
+  void* v_cache;
+  const int32_t* pairs;
+  size_t block_bytes;  // bytes of one block in one pool
+};
+
+struct DecodeArgs {
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const void* q;
+  void* out;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  int32_t* counters;  // [0] work queue, [1] finished waves, [2..] per (seq, kv head) partitions done
+  float* part_ml;     // [num_seqs][num_q_heads][max_parts][2]  (running max in log2 units, sum)
+  float* part_acc;    // [num_seqs][num_q_heads][max_parts][head_dim]
+  float scale_log2;   // softmax scale * log2(e)
+  int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq;
+  int32_t part_tokens, max_parts, total_waves;
+};
+
+struct DecodeWorkspace {
+  size_t counters_off, ml_off, acc_off, total;
+};
+
+// Record the message of a failed call for pa_last_error(); returns code.
+int set_error(int code, const char* fmt, ...);
+
+DecodeWorkspace decode_workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,
+                                        int64_t max_parts);
+
+hipError_t launch_store_kv(const StoreArgs& a, int kv_kind, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyArgs& a, int num_pairs, hipStream_t s);
+// Returns hipErrorInvalidValue for a combination without a compiled kernel.
+hipError_t launch_decode(const DecodeArgs& a, int kv_kind, int head_dim, int block_size, int group,
+                         int64_t upper_items, hipStream_t s);
+
+}  // namespace pa

@@ -1,0 +1,168 @@
+"""Lay a generated workload onto the GPU through libpa (product side).
+
+Allocation goes through libpa's own host block manager; pools are filled by
+pa_store_kv; the step then runs store -> attention.  Allocation order:
+sequences in listed order, each taking slots for its cached tokens and then
+for the tokens of the step.  Block-table rows are padded with a block that
+no sequence holds.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import binding as pa
+
+
+def _t(x: np.ndarray, device, dtype=None) -> torch.Tensor:
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        t = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(x)
+    if dtype is not None and t.dtype != dtype:
+        t = t.to(dtype)
+    return t.to(device)
+
+
+def _table_rows(rows: List[list], pad: int, width: Optional[int] = None) -> np.ndarray:
+    w = max([1] + [len(r) for r in rows]) if width is None else width
+    out = np.full((len(rows), w), pad, dtype=np.int32)
+    for i, r in enumerate(rows):
+        out[i, :len(r)] = r
+    return out
+
+
+@dataclass
+class GpuBatch:
+    batch: object
+    cache: pa.KVCache
+    bm: pa.BlockManager
+    tables: List[list]
+    pad: int
+    prior_slots: torch.Tensor
+    k_prior: torch.Tensor
+    v_prior: torch.Tensor
+    step_slots: torch.Tensor
+    k_step: torch.Tensor
+    v_step: torch.Tensor
+    dec: dict = field(default_factory=dict)
+    chunk: dict = field(default_factory=dict)
+
+
+def prepare(batch, device="cuda", fill=True) -> GpuBatch:
+    """Allocate, upload and (if ``fill``) store the cached tokens of a PagedBatch."""
+    bm = pa.BlockManager(batch.num_blocks, batch.block_size, batch.free_order)
+    prior, step = [], []
+    for i in range(batch.num_seqs):
+        s = bm.seq_new()
+        prior.append(bm.append(s, int(batch.prior_lens[i])))
+        step.append(bm.append(s, int(batch.new_lens[i])))
+    tables = [bm.block_table(i) for i in range(batch.num_seqs)]
+    pad = bm.unused_block()
+    off = batch.tok_offsets
+    pidx, sidx = [], []
+    for i in range(batch.num_seqs):
+        a, p, n = int(off[i]), int(batch.prior_lens[i]), int(batch.new_lens[i])
+        pidx.append(np.arange(a, a + p))
+        sidx.append(np.arange(a + p, a + p + n))
+    pidx = np.concatenate(pidx).astype(np.int64)
+    sidx = np.concatenate(sidx).astype(np.int64)
+    cache = pa.alloc_cache(batch.num_blocks, batch.num_kv_heads, batch.block_size, batch.head_dim,
+                           batch.kv_dtype, device=device, k_scale=batch.k_scale, v_scale=batch.v_scale)
+    g = GpuBatch(batch, cache, bm, tables, pad,
+                 _t(np.concatenate(prior).astype(np.int32), device), _t(batch.k[pidx], device),
+                 _t(batch.v[pidx], device),
+                 _t(np.concatenate(step).astype(np.int32), device), _t(batch.k[sidx], device),
+                 _t(batch.v[sidx], device))
+    dec = np.flatnonzero(~batch.is_chunk)
+    if len(dec):
+        lens = batch.total_lens[dec]
+        g.dec = dict(idx=dec, q=_t(batch.q_decode, device),
+                     table=_t(_table_rows([tables[i] for i in dec], pad), device),
+                     lens=_t(lens.astype(np.int32), device), max_len=int(lens.max()), host_lens=lens)
+    ch = np.flatnonzero(batch.is_chunk)
+    if len(ch):
+        ql = batch.new_lens[ch]
+        cu = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+        tl = batch.total_lens[ch]
+        g.chunk = dict(idx=ch, q=_t(batch.q_chunk, device), cu=_t(cu, device),
+                       seq_lens=_t(tl.astype(np.int32), device),
+                       table=_t(_table_rows([tables[i] for i in ch], pad), device),
+                       max_q=int(ql.max()), max_seq=int(tl.max()), host_prefix=(tl - ql), host_q=ql)
+    if fill:
+        fill_prior(g)
+    return g
+
+
+def fill_prior(g: GpuBatch) -> None:
+    if g.prior_slots.numel():
+        pa.store_kv(g.cache, g.k_prior, g.v_prior, g.prior_slots)
+
+
+def store_step(g: GpuBatch) -> None:
+    if g.step_slots.numel():
+        pa.store_kv(g.cache, g.k_step, g.v_step, g.step_slots)
+
+
+def decode_step(g: GpuBatch, out=None, partition_tokens=0, workspace=None) -> torch.Tensor:
+    d = g.dec
+    return pa.decode(g.cache, d["q"], d["table"], d["lens"], d["max_len"], g.batch.scale, out=out,
+                     partition_tokens=partition_tokens, workspace=workspace)
+
+
+def chunk_step(g: GpuBatch, out=None) -> torch.Tensor:
+    c = g.chunk
+    return pa.prefill_chunk(g.cache, c["q"], c["cu"], c["seq_lens"], c["table"], c["max_q"], c["max_seq"],
+                            g.batch.scale, out=out)
+
+
+@dataclass
+class GpuFork:
+    fb: object
+    cache: pa.KVCache
+    bm: pa.BlockManager
+    beams: list
+    pad: int
+    copy_pairs: np.ndarray
+    step_slots: np.ndarray   # [steps, beams]
+    snap_before_divergence: Optional[torch.Tensor] = None
+
+
+def run_fork(fb, device="cuda", snapshot=None) -> GpuFork:
+    """Store the shared prompt, fork into beams, then append the beams' tokens
+    one step at a time: each step's copy pairs are copied before its store.
+    ``snapshot(cache, beams, bm)`` is called right after the fork."""
+    bm = pa.BlockManager(fb.num_blocks, fb.block_size, fb.free_order)
+    parent = bm.seq_new()
+    shared = bm.append(parent, fb.shared_len)
+    cache = pa.alloc_cache(fb.num_blocks, fb.num_kv_heads, fb.block_size, fb.head_dim, fb.kv_dtype,
+                           device=device, k_scale=fb.k_scale, v_scale=fb.v_scale)
+    pa.store_kv(cache, _t(fb.k_shared, device), _t(fb.v_shared, device), _t(shared.astype(np.int32), device))
+    beams = [parent] + [bm.fork(parent) for _ in range(fb.beams - 1)]
+    if snapshot is not None:
+        snapshot(cache, beams, bm)
+    pairs_all, slots_all = [], []
+    kb = _t(fb.k_beam, device)
+    vb = _t(fb.v_beam, device)
+    for t in range(fb.steps):
+        slots = np.array([bm.append(b, 1)[0] for b in beams], dtype=np.int32)
+        pairs = bm.take_copies()
+        if len(pairs):
+            pa.copy_blocks(cache, _t(pairs.astype(np.int32), device))
+        pa.store_kv(cache, kb[t], vb[t], _t(slots, device))
+        pairs_all.append(pairs)
+        slots_all.append(slots)
+    return GpuFork(fb, cache, bm, beams, bm.unused_block(), np.concatenate(pairs_all).reshape(-1, 2),
+                   np.stack(slots_all))
+
+
+def fork_decode(gf: GpuFork, device="cuda", out=None, partition_tokens=0, workspace=None) -> torch.Tensor:
+    bm = gf.bm
+    table = _t(bm.block_tables(gf.beams, gf.pad), device)
+    lens = np.array([bm.seq_len(b) for b in gf.beams], dtype=np.int32)
+    return pa.decode(gf.cache, _t(gf.fb.q, device), table, _t(lens, device), int(lens.max()), gf.fb.scale,
+                     out=out, partition_tokens=partition_tokens, workspace=workspace)

@@ -1,0 +1,189 @@
+"""CPU checks of libpa's C ABI: it loads, exports every symbol include/pa.h
+declares, rejects bad arguments on the host (before any HIP call, so these
+run without a GPU), and its host block manager makes the same decisions as
+the oracle's."""
+import ctypes as C
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+from oracle.block_manager import BlockManager as OracleBM, Sequence as OracleSeq
+from paged_kv_attention_26_amd import _lib as L
+from paged_kv_attention_26_amd.binding import BlockManager as NativeBM
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libpa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    lib = L.lib()
+    names = declared_functions()
+    assert "pa_decode" in names and "pa_bm_create" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == {s[0] for s in L.SIGNATURES}
+
+
+FAKE = 0x10000          # never dereferenced: every call below is rejected first
+
+
+def cache(**kw):
+    d = dict(k_cache=FAKE, v_cache=FAKE, k_scale=None, v_scale=None, num_blocks=8, num_kv_heads=2,
+             block_size=16, head_dim=64, dtype=L.PA_BF16)
+    d.update(kw)
+    return L.PaKvCache(**d)
+
+
+def decode_call(c, **kw):
+    a = dict(q=FAKE, q_dtype=L.PA_BF16, out=FAKE, out_dtype=L.PA_BF16, S=2, Hq=4, scale=0.125, table=FAKE,
+             max_blocks=4, lens=FAKE, max_ctx=64, part=0, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return L.lib().pa_decode(C.byref(c) if c is not None else None, a["q"], a["q_dtype"], a["out"],
+                             a["out_dtype"], a["S"], a["Hq"], a["scale"], a["table"], a["max_blocks"], a["lens"],
+                             a["max_ctx"], a["part"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(c=None), L.PA_ERR_NULL),
+    (dict(c=cache(k_cache=None)), L.PA_ERR_NULL),
+    (dict(c=cache(dtype=7)), L.PA_ERR_DTYPE),
+    (dict(c=cache(head_dim=96)), L.PA_ERR_UNSUPPORTED),
+    (dict(c=cache(block_size=8)), L.PA_ERR_UNSUPPORTED),
+    (dict(c=cache(dtype=L.PA_FP8_E4M3)), L.PA_ERR_NULL),            # fp8 without scales
+    (dict(c=cache(k_scale=FAKE, v_scale=FAKE)), L.PA_ERR_DTYPE),     # scales on a bf16 cache
+    (dict(c=cache(), Hq=3), L.PA_ERR_SHAPE),                         # Hq % Hkv
+    (dict(c=cache(), Hq=32), L.PA_ERR_UNSUPPORTED),                  # group 16
+    (dict(c=cache(), q_dtype=L.PA_F32), L.PA_ERR_DTYPE),
+    (dict(c=cache(dtype=L.PA_F32)), L.PA_ERR_DTYPE),                 # bf16 q on an f32 cache
+    (dict(c=cache(), max_blocks=3), L.PA_ERR_SHAPE),                 # 64 tokens need 4 blocks
+    (dict(c=cache(), part=100), L.PA_ERR_SHAPE),
+    (dict(c=cache(), part=2048), L.PA_ERR_SHAPE),                    # > 64 blocks of 16
+    (dict(c=cache(), ws_bytes=16), L.PA_ERR_WORKSPACE),
+    (dict(c=cache(), lens=None), L.PA_ERR_NULL),
+    (dict(c=cache(), S=-1), L.PA_ERR_SHAPE),
+    (dict(c=cache(), scale=float("nan")), L.PA_ERR_SHAPE),
+])
+def test_decode_rejects_bad_arguments(kw, code):
+    c = kw.pop("c")
+    assert decode_call(c, **kw) == code
+    assert L.lib().pa_last_error()
+
+
+def test_decode_with_no_sequences_is_a_noop():
+    assert decode_call(cache(), S=0) == L.PA_OK
+
+
+def test_store_and_copy_reject_bad_arguments():
+    lib = L.lib()
+    c = cache()
+    assert lib.pa_store_kv(None, FAKE, FAKE, L.PA_BF16, FAKE, 4, None) == L.PA_ERR_NULL
+    assert lib.pa_store_kv(C.byref(c), FAKE, FAKE, L.PA_F32, FAKE, 4, None) == L.PA_ERR_DTYPE
+    assert lib.pa_store_kv(C.byref(c), None, FAKE, L.PA_BF16, FAKE, 4, None) == L.PA_ERR_NULL
+    assert lib.pa_store_kv(C.byref(c), FAKE, FAKE, L.PA_BF16, FAKE, -1, None) == L.PA_ERR_SHAPE
+    assert lib.pa_store_kv(C.byref(c), FAKE, FAKE, L.PA_BF16, FAKE, 0, None) == L.PA_OK
+    f8 = cache(dtype=L.PA_FP8_E4M3, k_scale=FAKE, v_scale=FAKE)
+    assert lib.pa_store_kv(C.byref(f8), FAKE, FAKE, L.PA_FP8_E4M3, FAKE, 4, None) == L.PA_ERR_DTYPE
+    assert lib.pa_copy_blocks(C.byref(c), None, 3, None) == L.PA_ERR_NULL
+    assert lib.pa_copy_blocks(C.byref(c), FAKE, -2, None) == L.PA_ERR_SHAPE
+    assert lib.pa_copy_blocks(C.byref(c), FAKE, 0, None) == L.PA_OK
+
+
+def test_prefill_rejects_bad_arguments():
+    lib = L.lib()
+    c = cache(head_dim=128, num_kv_heads=8)
+    args = [FAKE, L.PA_BF16, FAKE, L.PA_BF16, 2, 32, 0.088, FAKE, FAKE, FAKE, 64, 512, 1024, None]
+    assert lib.pa_prefill_chunk(None, *args) == L.PA_ERR_NULL
+    bad = list(args); bad[5] = 30                                      # Hq % Hkv
+    assert lib.pa_prefill_chunk(C.byref(c), *bad) == L.PA_ERR_SHAPE
+    bad = list(args); bad[1] = L.PA_F32
+    assert lib.pa_prefill_chunk(C.byref(c), *bad) in (L.PA_ERR_DTYPE, L.PA_ERR_UNSUPPORTED)
+    bad = list(args); bad[10] = 8                                      # table narrower than max_seq_len
+    assert lib.pa_prefill_chunk(C.byref(c), *bad) in (L.PA_ERR_SHAPE, L.PA_ERR_UNSUPPORTED)
+
+
+def test_workspace_size_query():
+    lib = L.lib()
+    a = lib.pa_decode_workspace_bytes(32, 32, 128, 4096, 512)
+    b = lib.pa_decode_workspace_bytes(32, 32, 128, 8192, 512)
+    assert 0 < a < b
+    assert lib.pa_decode_workspace_bytes(-1, 32, 128, 4096, 512) == 0
+    assert lib.pa_decode_workspace_bytes(32, 32, 128, 4096, 100) == 0
+    # m, l and an fp32 accumulator per (sequence, head, partition) fit
+    assert a >= 32 * 32 * 8 * (128 + 2) * 4
+
+
+# ------------------------------------------- native block manager == oracle
+def _trace(seed, steps=300, pool=40, B=16):
+    """Drive both managers with the same random append / fork / release trace
+    and compare every decision: slots, copy pairs, tables, counts."""
+    rng = random.Random(seed)
+    order = np.random.default_rng(seed).permutation(pool)
+    o = OracleBM(pool, B, order)
+    n = NativeBM(pool, B, order)
+    oseqs = {0: OracleSeq(o, 0)}
+    nseqs = {0: n.seq_new()}
+    for _ in range(steps):
+        sid = rng.choice(sorted(oseqs))
+        op = rng.random()
+        if op < 0.65:
+            k = rng.randint(1, 40)
+            try:
+                want = oseqs[sid].append_slots(k)
+            except MemoryError:
+                want = None
+            if want is None:
+                with pytest.raises(MemoryError):
+                    n.append(nseqs[sid], k)
+                o.take_copies(), n.take_copies()
+                oseqs[sid].release(); n.release(nseqs[sid])
+                continue
+            got = n.append(nseqs[sid], k).tolist()
+            assert got == want
+        elif op < 0.85 and len(oseqs) < 12:
+            new = max(oseqs) + 1
+            oseqs[new] = oseqs[sid].fork(new)
+            nseqs[new] = n.fork(nseqs[sid])
+        elif len(oseqs) > 1:
+            oseqs.pop(sid).release()
+            n.release(nseqs.pop(sid))
+        assert n.take_copies().tolist() == [list(p) for p in o.take_copies()]
+        assert n.used_blocks == o.used_blocks
+        for s in oseqs:
+            assert n.block_table(nseqs[s]) == oseqs[s].block_table
+            assert n.seq_len(nseqs[s]) == oseqs[s].length
+        assert [n.ref_count(b) for b in range(pool)] == o.ref_count
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_native_block_manager_matches_oracle(seed):
+    _trace(seed)
+
+
+def test_native_block_manager_fork_demo():
+    n = NativeBM(64, 16)
+    s = n.seq_new()
+    n.append(s, 100)
+    assert n.used_blocks == 7
+    kids = [n.fork(s) for _ in range(4)]
+    assert n.used_blocks == 7
+    for k in kids:
+        n.append(k, 1)
+    assert n.used_blocks == 11
+    pairs = n.take_copies()
+    assert len(pairs) == 4 and len(set(pairs[:, 0].tolist())) == 1
+
+
+def test_native_block_manager_rejects_bad_free_order():
+    with pytest.raises(L.PaError):
+        NativeBM(4, 16, [0, 1, 1, 3])

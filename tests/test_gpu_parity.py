@@ -1,0 +1,205 @@
+"""GPU parity of libpa against the CPU oracle (needs an MI355X).
+
+Store and copy are compared bit for bit over the whole pool (untouched slots
+must keep their NaN poison); attention within max-abs 1e-4 (fp32 cache),
+2e-2 (bf16) and 6e-2 (fp8) of the fp64 oracle.  Both sides make the same
+allocation decisions (the native block manager equals the oracle's, checked
+on the CPU), and every input comes from the seeded generators.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests import oracle_setup as OS
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_kv_attention_26_amd import _lib
+    _lib.lib()
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bits(t: torch.Tensor, kv: str) -> np.ndarray:
+    t = t.detach().cpu()
+    if kv == "f32":
+        return t.view(torch.int32).numpy().view(np.uint32)
+    if kv == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def oracle_bits(a: np.ndarray, kv: str) -> np.ndarray:
+    return a.view(np.uint32) if kv == "f32" else a
+
+
+def out_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def edge_batch(kv="bf16", B=16):
+    rng = np.random.default_rng(77)
+    lens = np.array([1, 2, 15, 16, 17, 63, 64, 65, 511, 512, 513, 1024, 1025, 0, 129, 4100])
+    prior = np.maximum(lens - 1, 0)
+    new = (lens > 0).astype(np.int64)
+    io = "f32" if kv == "f32" else "bf16"
+    Hq, Hkv, d = (8, 2, 64) if kv == "f32" else (32, 8, 128)
+    return W.paged_batch(f"edge-{kv}-b{B}", 77, kv_dtype=kv, io_dtype=io, Hq=Hq, Hkv=Hkv, d=d, B=B,
+                         prior_lens=prior, new_lens=new, is_chunk=np.zeros(len(lens), bool), rng=rng)
+
+
+SMALL = {
+    "c1": lambda: W.config1(),
+    "c2s": lambda: W.config2(small=True),
+    "c3s16": lambda: W.config3(16, small=True),
+    "c3s32": lambda: W.config3(32, small=True),
+    "edge16": lambda: edge_batch("bf16", 16),
+    "edge32": lambda: edge_batch("bf16", 32),
+    "edge-f32": lambda: edge_batch("f32", 16),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_store_is_bit_exact_over_the_whole_pool(name):
+    from paged_kv_attention_26_amd import runner
+    say(f"[gpu] store {name}")
+    batch = SMALL[name]()
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    torch.cuda.synchronize()
+    st = OS.build(batch)
+    assert g.tables == st.tables
+    assert np.array_equal(bits(g.cache.k_cache, batch.kv_dtype), oracle_bits(st.kc, batch.kv_dtype))
+    assert np.array_equal(bits(g.cache.v_cache, batch.kv_dtype), oracle_bits(st.vc, batch.kv_dtype))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("part", [0, 64, 128])
+def test_decode_matches_oracle(name, part):
+    from paged_kv_attention_26_amd import runner
+    say(f"[gpu] decode {name} partition {part}")
+    batch = SMALL[name]()
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    out = runner.decode_step(g, partition_tokens=part)
+    torch.cuda.synchronize()
+    ref = OS.decode_ref(batch, OS.build(batch))
+    got = out_f64(out)
+    assert np.all(np.isfinite(got))
+    err = np.max(np.abs(got - ref))
+    say(f"      max abs err {err:.3e}")
+    assert err < TOL[batch.kv_dtype]
+
+
+def test_decode_repeated_calls_reuse_the_workspace():
+    """The workspace counters reset themselves: back-to-back calls on one
+    workspace give bit-identical results."""
+    from paged_kv_attention_26_amd import binding as pa, runner
+    batch = W.config3(16, small=True)
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    d = g.dec
+    ws = pa.decode_workspace(len(d["idx"]), batch.num_q_heads, batch.head_dim, d["max_len"], 64)
+    outs = [runner.decode_step(g, partition_tokens=64, workspace=ws).clone() for _ in range(5)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    assert int(ws[:8].view(torch.int32).abs().sum()) == 0
+
+
+def test_block_permutation_leaves_output_bit_identical():
+    from paged_kv_attention_26_amd import runner
+    a = W.config2(small=True)
+    b = W.config2(small=True)
+    b.free_order = np.random.default_rng(99).permutation(b.num_blocks)
+    ga, gb = runner.prepare(a), runner.prepare(b)
+    runner.store_step(ga), runner.store_step(gb)
+    assert ga.tables != gb.tables
+    oa, ob = runner.decode_step(ga), runner.decode_step(gb)
+    torch.cuda.synchronize()
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+
+
+def test_partition_size_changes_output_only_by_rounding():
+    from paged_kv_attention_26_amd import runner
+    batch = W.config3(16, small=True)
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    outs = [out_f64(runner.decode_step(g, partition_tokens=p)) for p in (64, 256, 1024)]
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) < 1e-2
+
+
+@pytest.mark.parametrize("small", [True, False])
+def test_fp8_fork_store_copy_and_decode(small):
+    from paged_kv_attention_26_amd import runner
+    say(f"[gpu] fp8 fork small={small}")
+    fb = W.config5(small=small)
+    snap = {}
+
+    def before(cache, beams, bm):
+        table = torch.from_numpy(bm.block_tables(beams, bm.unused_block())).cuda()
+        lens = torch.full((len(beams),), fb.shared_len, dtype=torch.int32, device="cuda")
+        q = torch.from_numpy(np.repeat(fb.q[:1], len(beams), 0).view(np.int16)).view(torch.bfloat16).cuda()
+        from paged_kv_attention_26_amd import binding as pa
+        snap["out"] = pa.decode(cache, q, table, lens, fb.shared_len, fb.scale).clone()
+
+    gf = runner.run_fork(fb, snapshot=before)
+    out = runner.fork_decode(gf)
+    torch.cuda.synchronize()
+    st = OS.build_fork(fb)
+    # copy-on-write decisions and block contents, bit for bit
+    assert gf.copy_pairs.tolist() == [list(p) for p in st.copy_pairs]
+    assert len(gf.copy_pairs) == fb.beams - 1
+    assert np.array_equal(bits(gf.cache.k_cache, "fp8"), st.kc)
+    assert np.array_equal(bits(gf.cache.v_cache, "fp8"), st.vc)
+    # forked beams read identical blocks before divergence: identical outputs
+    b0 = snap["out"][0].view(torch.int16)
+    for b in range(1, fb.beams):
+        assert torch.equal(snap["out"][b].view(torch.int16), b0)
+    ref = OS.fork_decode_ref(fb, st)
+    err = np.max(np.abs(out_f64(out) - ref))
+    say(f"      max abs err {err:.3e}")
+    assert err < TOL["fp8"]
+
+
+def test_fp8_codes_round_trip_through_store_and_decode():
+    """Values that are exact e4m3 numbers (scale 1) are stored as their codes
+    and a one-token decode returns them exactly: checks the device encoder
+    and the hardware e4m3 -> fp32 conversion on every finite code."""
+    from oracle import fp8_e4m3
+    from paged_kv_attention_26_amd import binding as pa
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = fp8_e4m3.decode(codes)                                   # 254 exact values
+    row = np.zeros((1, 2, 128), np.float32)
+    row.reshape(-1)[:254] = vals
+    bits_in = W.to_bf16_bits(row)                                   # exact in bf16
+    assert np.array_equal(W.bf16_bits_to_f32(bits_in).astype(np.float64), row.astype(np.float64))
+    one = np.ones(2, np.float32)
+    cache = pa.alloc_cache(4, 2, 16, 128, "fp8", k_scale=one, v_scale=one)
+    x = torch.from_numpy(bits_in.view(np.int16)).view(torch.bfloat16).cuda()
+    pa.store_kv(cache, x, x, torch.tensor([32], dtype=torch.int32, device="cuda"))   # block 2, offset 0
+    k = cache.k_cache.cpu().numpy()
+    v = cache.v_cache.cpu().numpy()
+    assert np.array_equal(k[2, :, 0, :].reshape(-1)[:254], codes)
+    assert np.array_equal(v[2, :, :, 0].reshape(-1)[:254], codes)
+    # a one-token context returns that token's value exactly
+    q = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
+    table = torch.tensor([[2]], dtype=torch.int32, device="cuda")
+    out = pa.decode(cache, q, table, torch.tensor([1], dtype=torch.int32, device="cuda"), 1, 0.088)
+    got = out.float().cpu().numpy().astype(np.float64)              # [1, 8, 128]
+    want = np.repeat(row.astype(np.float64), 4, axis=1)             # kv head h -> q heads 4h..4h+3
+    assert np.array_equal(got[0], want[0])
