@@ -89,7 +89,7 @@ DecodeWorkspace decode_workspace_layout(int64_t S, int64_t Hq, int64_t D, int64_
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   DecodeWorkspace w;
   w.counters_off = 0;
-  w.ml_off = up(size_t(2 + S * Hq) * sizeof(int32_t));
+  w.ml_off = up(2 * sizeof(int32_t));
   w.acc_off = w.ml_off + up(size_t(S * Hq * max_parts * 2) * sizeof(float));
   w.total = w.acc_off + up(size_t(S * Hq * max_parts * D) * sizeof(float));
   return w;

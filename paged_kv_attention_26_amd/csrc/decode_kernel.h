@@ -30,16 +30,27 @@
 //    consecutive tokens of one head dimension; v_dot2_f32_bf16 with the bf16
 //    probabilities accumulates in fp32 with no cross-lane reduction until
 //    the end of the item.
+//  * Loads are software-pipelined: the next step's K tile is issued right
+//    after this step's scores, its V tile right after this step's PV, so a
+//    wave always has one tile in flight while it computes.
 //  * Split-K: an item of a multi-partition sequence writes (max, sum, acc)
-//    to the workspace; the wave that finishes the last partition of a
-//    (sequence, kv head) merges them by log-sum-exp rescaling.  Counters
-//    reset themselves, so the workspace needs zero-filling only once.
+//    to the workspace and a small reduce kernel merges the partitions by
+//    log-sum-exp rescaling (the kernel boundary orders the two, which costs
+//    less than a device-scope fence per item).  The queue counters reset
+//    themselves, so the workspace needs zero-filling only once.
 #pragma once
 
 #include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
+
+#ifndef PA_DECODE_STEP_TOKENS
+#define PA_DECODE_STEP_TOKENS 64
+#endif
+#ifndef PA_DECODE_WAVES_ATTR
+#define PA_DECODE_WAVES_ATTR
+#endif
 
 namespace pa {
 
@@ -56,12 +67,13 @@ struct DecCfg {
   static constexpr int DPL = 64 / LPD;                            // head dims per value load
   static constexpr int KLB = B / RPL;                             // key loads per block
   static constexpr int VLB = D / DPL;                             // value loads per block
-  static constexpr int CH = 64;                                   // tokens per step
+  static constexpr int CH = PA_DECODE_STEP_TOKENS > B ? PA_DECODE_STEP_TOKENS : B;   // tokens per step (<= 64)
   static constexpr int BPC = CH / B;                              // blocks per step
   using LoadT = typename std::conditional<LBYTES == 16, uint4, uint2>::type;
   static_assert(LPR >= G && LPR <= 64 && (64 % LPR) == 0, "key row mapping");
   static_assert(LPD >= 1 && LPD <= 64, "value row mapping");
   static_assert(D % DPL == 0 && B % RPL == 0, "tile mapping");
+  static_assert(CH <= 64 && CH % B == 0, "a step is at most one token per lane");
 };
 
 template <int KV>
@@ -75,7 +87,7 @@ __device__ __forceinline__ void load_pairs(const uint2& x, uint32_t p[4]) {
 }
 
 template <int KV, int D, int B, int G>
-__global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(256) PA_DECODE_WAVES_ATTR decode_kernel(DecodeArgs a) {
   using C = DecCfg<KV, D, B, G>;
   using LoadT = typename C::LoadT;
   extern __shared__ int s_prefix[];                       // [num_seqs + 1] partitions before each sequence
@@ -120,12 +132,16 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   const int vs = lane % C::LPD, vd = lane / C::LPD;       // value token segment, head-dim row
   const char* kpool = static_cast<const char*>(a.k_cache);
   const char* vpool = static_cast<const char*>(a.v_cache);
+  constexpr uint64_t kTile = uint64_t(B) * D * C::ES;     // bytes of one (block, kv head) tile
+  const uint32_t k_off = uint32_t((kr * D + kcol * C::EPL) * C::ES);
+  const uint32_t v_off = uint32_t((vd * B + vs * C::TPL) * C::ES);
 
+  int next = 0;
+  if (lane == 0) next = atomicAdd(&a.counters[0], 1);
   for (;;) {
-    int item = 0;
-    if (lane == 0) item = atomicAdd(&a.counters[0], 1);
-    item = __builtin_amdgcn_readlane(item, 0);
+    const int item = __builtin_amdgcn_readlane(next, 0);
     if (item >= total_items) break;
+    if (lane == 0) next = atomicAdd(&a.counters[0], 1);      // fetch the following item early
     const int gp = item / Hkv;
     const int kvh = item - gp * Hkv;
     int lo = 0, hi = S;
@@ -173,87 +189,98 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       for (int j = 0; j < C::VLB; ++j) acc[g][j] = 0.f;
     }
 
-    for (int cs = t_begin; cs < t_end; cs += C::CH) {
-      const int nb = min(C::BPC, (t_end - cs + B - 1) / B);
-      const int tb0 = (cs - t_begin) / B;
-      LoadT kreg[C::BPC][C::KLB];
-      LoadT vreg[C::BPC][C::VLB];
+    // Loads are unconditional so that the compiler can count them exactly
+    // (s_waitcnt vmcnt(n) instead of vmcnt(0) at every use): blocks past
+    // the end of the partition re-read its last block, the prefetch of the
+    // last step re-reads that step, and everything past t_end is masked.
+    LoadT kreg[C::BPC][C::KLB];
+    LoadT vreg[C::BPC][C::VLB];
+    const int last_blk = max(nblk - 1, 0);
+    const int nsteps = (t_end - t_begin + C::CH - 1) / C::CH;
+    // uniform tile base (SGPRs) + one 32-bit lane offset + immediate offsets
+    auto load_k = [&](int step) {
 #pragma unroll
       for (int k = 0; k < C::BPC; ++k) {
-        if (k < nb) {
-          const int blk = __builtin_amdgcn_readlane(tbl, tb0 + k);
-          const char* kt = kpool + (size_t(blk) * Hkv + kvh) * size_t(B * D * C::ES);
+        const uint32_t blk = uint32_t(__builtin_amdgcn_readlane(tbl, min(step * C::BPC + k, last_blk)));
+        const auto r = tile_rsrc(kpool + (uint64_t(blk) * uint32_t(Hkv) + uint32_t(kvh)) * kTile, uint32_t(kTile));
 #pragma unroll
-          for (int i = 0; i < C::KLB; ++i)
-            kreg[k][i] = *reinterpret_cast<const LoadT*>(kt + ((i * C::RPL + kr) * D + kcol * C::EPL) * C::ES);
-        }
+        for (int i = 0; i < C::KLB; ++i) buffer_load(r, k_off + uint32_t(i * C::RPL * D * C::ES), kreg[k][i]);
       }
+    };
+    auto load_v = [&](int step) {
 #pragma unroll
       for (int k = 0; k < C::BPC; ++k) {
-        if (k < nb) {
-          const int blk = __builtin_amdgcn_readlane(tbl, tb0 + k);
-          const char* vt = vpool + (size_t(blk) * Hkv + kvh) * size_t(B * D * C::ES);
+        const uint32_t blk = uint32_t(__builtin_amdgcn_readlane(tbl, min(step * C::BPC + k, last_blk)));
+        const auto r = tile_rsrc(vpool + (uint64_t(blk) * uint32_t(Hkv) + uint32_t(kvh)) * kTile, uint32_t(kTile));
 #pragma unroll
-          for (int j = 0; j < C::VLB; ++j)
-            vreg[k][j] = *reinterpret_cast<const LoadT*>(vt + ((j * C::DPL + vd) * B + vs * C::TPL) * C::ES);
-        }
+        for (int j = 0; j < C::VLB; ++j) buffer_load(r, v_off + uint32_t(j * C::DPL * B * C::ES), vreg[k][j]);
       }
+    };
 
-      // ---- scores
+    // Block ids and the query must be in registers before the first tile is
+    // requested; an explicit wait here keeps the compiler from waiting on
+    // every in-flight tile (vmcnt(0)) at the top of each step.
+    __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0) only
+    load_k(0);                                                // (re-reads block 0 when the item is empty)
+    load_v(0);
+    for (int st = 0; st < nsteps; ++st) {
+      const int cs = t_begin + st * C::CH;
+      const int nxt = min(st + 1, nsteps - 1);
+
+      // ---- scores (tokens past t_end are masked in the softmax)
 #pragma unroll
       for (int k = 0; k < C::BPC; ++k) {
-        if (k < nb) {
 #pragma unroll
-          for (int i = 0; i < C::KLB; ++i) {
-            float pt[G];
-            if constexpr (C::F32) {
-              const uint4 x = kreg[k][i];
-              const float kf[4] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
-                                   __uint_as_float(x.w)};
+        for (int i = 0; i < C::KLB; ++i) {
+          float pt[G];
+          if constexpr (C::F32) {
+            const uint4 x = kreg[k][i];
+            const float kf[4] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
+                                 __uint_as_float(x.w)};
 #pragma unroll
-              for (int j = 0; j < G; ++j)
-                pt[j] = fmaf(kf[3], qf[j][3], fmaf(kf[2], qf[j][2], fmaf(kf[1], qf[j][1], kf[0] * qf[j][0])));
-            } else {
-              uint32_t kp[4];
-              load_pairs<KV>(kreg[k][i], kp);
+            for (int j = 0; j < G; ++j)
+              pt[j] = fmaf(kf[3], qf[j][3], fmaf(kf[2], qf[j][2], fmaf(kf[1], qf[j][1], kf[0] * qf[j][0])));
+          } else {
+            uint32_t kp[4];
+            load_pairs<KV>(kreg[k][i], kp);
 #pragma unroll
-              for (int j = 0; j < G; ++j)
-                pt[j] = dot2_bf16(kp[3], qp[j][3],
-                                  dot2_bf16(kp[2], qp[j][2], dot2_bf16(kp[1], qp[j][1], dot2_bf16(kp[0], qp[j][0], 0.f))));
-            }
-            if constexpr (G >= 8) {
-#pragma unroll
-              for (int x = 0; x < 4; ++x) pt[x] += dpp<DPP_HALF_MIRROR>(pt[x + 4]);
-            }
-            if constexpr (G >= 4) {
-#pragma unroll
-              for (int x = 0; x < 2; ++x) pt[x] += dpp<DPP_QP_XOR3>(pt[x + 2]);
-            }
-            if constexpr (G >= 2) pt[0] += dpp<DPP_QP_XOR1>(pt[1]);
-            float sc = pt[0];
-#pragma unroll
-            for (int st = G; st < C::LPR; st *= 2) {
-              if constexpr (C::LPR == 16) {
-                if (st == 1) sc += dpp<DPP_ROW_ROR(1)>(sc);
-                else if (st == 2) sc += dpp<DPP_ROW_ROR(2)>(sc);
-                else if (st == 4) sc += dpp<DPP_ROW_ROR(4)>(sc);
-                else sc += dpp<DPP_ROW_ROR(8)>(sc);
-              } else {
-                sc += __shfl_xor(sc, st);
-              }
-            }
-            if (kcol < G) s_score[w][(k * B + i * C::RPL + kr) * G + gray] = sc * sl;
+            for (int j = 0; j < G; ++j)
+              pt[j] = dot2_bf16(kp[3], qp[j][3],
+                                dot2_bf16(kp[2], qp[j][2], dot2_bf16(kp[1], qp[j][1], dot2_bf16(kp[0], qp[j][0], 0.f))));
           }
+          if constexpr (G >= 8) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) pt[x] += dpp<DPP_HALF_MIRROR>(pt[x + 4]);
+          }
+          if constexpr (G >= 4) {
+#pragma unroll
+            for (int x = 0; x < 2; ++x) pt[x] += dpp<DPP_QP_XOR3>(pt[x + 2]);
+          }
+          if constexpr (G >= 2) pt[0] += dpp<DPP_QP_XOR1>(pt[1]);
+          float sc = pt[0];
+#pragma unroll
+          for (int sp = G; sp < C::LPR; sp *= 2) {
+            if constexpr (C::LPR == 16) {
+              if (sp == 1) sc += dpp<DPP_ROW_ROR(1)>(sc);
+              else if (sp == 2) sc += dpp<DPP_ROW_ROR(2)>(sc);
+              else if (sp == 4) sc += dpp<DPP_ROW_ROR(4)>(sc);
+              else sc += dpp<DPP_ROW_ROR(8)>(sc);
+            } else {
+              sc += __shfl_xor(sc, sp);
+            }
+          }
+          if (kcol < G) s_score[w][(k * B + i * C::RPL + kr) * G + gray] = sc * sl;
         }
       }
+      load_k(nxt);                                            // next step's keys fly during softmax + PV
       wave_lds_sync();
 
       // ---- online softmax over this step, one token per lane
-      const bool valid = cs + lane < t_end;
+      const bool valid = lane < C::CH && cs + lane < t_end;
       float pv[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float sv = valid ? s_score[w][lane * G + g] : -INFINITY;
+        const float sv = valid ? s_score[w][min(lane, C::CH - 1) * G + g] : -INFINITY;
         const float mn = fmaxf(m_run[g], wave_max(sv));
         const float al = exp2f(m_run[g] - mn);
         pv[g] = exp2f(sv - mn);
@@ -262,67 +289,68 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         for (int j = 0; j < C::VLB; ++j) acc[g][j] *= al;
         m_run[g] = mn;
       }
-      if constexpr (C::F32) {
+      if (lane < C::CH) {
+        if constexpr (C::F32) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) reinterpret_cast<float*>(s_p[w])[g * C::CH + lane] = pv[g];
-      } else {
+          for (int g = 0; g < G; ++g) reinterpret_cast<float*>(s_p[w])[g * C::CH + lane] = pv[g];
+        } else {
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-          reinterpret_cast<uint16_t*>(s_p[w])[g * C::CH + lane] = uint16_t(pack_bf16x2(pv[g], 0.f) & 0xFFFFu);
+          for (int g = 0; g < G; ++g)
+            reinterpret_cast<uint16_t*>(s_p[w])[g * C::CH + lane] = uint16_t(pack_bf16x2(pv[g], 0.f) & 0xFFFFu);
+        }
       }
       wave_lds_sync();
 
-      // ---- PV
+      // ---- PV (values of tokens past t_end may be NaN poison: zeroed by select)
 #pragma unroll
       for (int k = 0; k < C::BPC; ++k) {
-        if (k < nb) {
-          const int tok0 = k * B + vs * C::TPL;            // step-relative first token of this lane's segment
-          const bool tail = cs + k * B + B > t_end;         // block holds tokens past the end
-          if constexpr (C::F32) {
-            float pf[G][4];
+        const int tok0 = k * B + vs * C::TPL;              // step-relative first token of this lane's segment
+        const bool tail = cs + k * B + B > t_end;           // block holds tokens past the end
+        if constexpr (C::F32) {
+          float pf[G][4];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-              const float4 t = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(s_p[w]) + g * C::CH + tok0);
-              pf[g][0] = t.x; pf[g][1] = t.y; pf[g][2] = t.z; pf[g][3] = t.w;
+          for (int g = 0; g < G; ++g) {
+            const float4 t = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(s_p[w]) + g * C::CH + tok0);
+            pf[g][0] = t.x; pf[g][1] = t.y; pf[g][2] = t.z; pf[g][3] = t.w;
+          }
+#pragma unroll
+          for (int j = 0; j < C::VLB; ++j) {
+            const uint4 x = vreg[k][j];
+            float v[4] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w)};
+            if (tail) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = (cs + tok0 + e < t_end) ? v[e] : 0.f;
             }
 #pragma unroll
-            for (int j = 0; j < C::VLB; ++j) {
-              const uint4 x = vreg[k][j];
-              float v[4] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w)};
-              if (tail) {
+            for (int g = 0; g < G; ++g)
+              acc[g][j] = fmaf(v[3], pf[g][3], fmaf(v[2], pf[g][2], fmaf(v[1], pf[g][1], fmaf(v[0], pf[g][0], acc[g][j]))));
+          }
+        } else {
+          uint32_t pp[G][4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (cs + tok0 + e < t_end) ? v[e] : 0.f;
+          for (int g = 0; g < G; ++g) {
+            const uint4 t = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(s_p[w]) + g * C::CH + tok0);
+            pp[g][0] = t.x; pp[g][1] = t.y; pp[g][2] = t.z; pp[g][3] = t.w;
+          }
+#pragma unroll
+          for (int j = 0; j < C::VLB; ++j) {
+            uint32_t vp[4];
+            load_pairs<KV>(vreg[k][j], vp);
+            if (tail) {
+#pragma unroll
+              for (int m = 0; m < 4; ++m) {
+                const int t = cs + tok0 + 2 * m;
+                vp[m] &= (t < t_end ? 0x0000FFFFu : 0u) | (t + 1 < t_end ? 0xFFFF0000u : 0u);
               }
-#pragma unroll
-              for (int g = 0; g < G; ++g)
-                acc[g][j] = fmaf(v[3], pf[g][3], fmaf(v[2], pf[g][2], fmaf(v[1], pf[g][1], fmaf(v[0], pf[g][0], acc[g][j]))));
-            }
-          } else {
-            uint32_t pp[G][4];
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-              const uint4 t = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(s_p[w]) + g * C::CH + tok0);
-              pp[g][0] = t.x; pp[g][1] = t.y; pp[g][2] = t.z; pp[g][3] = t.w;
             }
 #pragma unroll
-            for (int j = 0; j < C::VLB; ++j) {
-              uint32_t vp[4];
-              load_pairs<KV>(vreg[k][j], vp);
-              if (tail) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                  const int t = cs + tok0 + 2 * m;
-                  vp[m] &= (t < t_end ? 0x0000FFFFu : 0u) | (t + 1 < t_end ? 0xFFFF0000u : 0u);
-                }
-              }
-#pragma unroll
-              for (int g = 0; g < G; ++g)
-                acc[g][j] = dot2_bf16(vp[3], pp[g][3], dot2_bf16(vp[2], pp[g][2],
-                            dot2_bf16(vp[1], pp[g][1], dot2_bf16(vp[0], pp[g][0], acc[g][j]))));
-            }
+            for (int g = 0; g < G; ++g)
+              acc[g][j] = dot2_bf16(vp[3], pp[g][3], dot2_bf16(vp[2], pp[g][2],
+                          dot2_bf16(vp[1], pp[g][1], dot2_bf16(vp[0], pp[g][0], acc[g][j]))));
           }
         }
       }
+      load_v(nxt);                                            // next step's values fly during its scores
     }
 
     // ---- finish the item
@@ -355,65 +383,21 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
           }
         }
       }
-      continue;
-    }
-
-    // multi-partition sequence: publish this partition, the last one merges
+    } else {
+      // multi-partition sequence: publish this partition for the reduce kernel
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const size_t base = (size_t(seq) * Hq + kvh * G + g) * a.max_parts + part;
-      if (lane == 0) {
-        a.part_ml[2 * base] = m_run[g];
-        a.part_ml[2 * base + 1] = l[g];
-      }
-      if (vs == 0) {
+      for (int g = 0; g < G; ++g) {
+        const size_t base = (size_t(seq) * Hq + kvh * G + g) * a.max_parts + part;
+        if (lane == 0) {
+          a.part_ml[2 * base] = m_run[g];
+          a.part_ml[2 * base + 1] = l[g];
+        }
+        if (vs == 0) {
 #pragma unroll
-        for (int j = 0; j < C::VLB; ++j) a.part_acc[base * D + j * C::DPL + vd] = acc[g][j];
-      }
-    }
-    __threadfence();
-    int done = 0;
-    int* ctr = &a.counters[2 + seq * Hkv + kvh];
-    if (lane == 0) done = atomicAdd(ctr, 1);
-    done = __builtin_amdgcn_readlane(done, 0);
-    if (done != np - 1) continue;
-    __threadfence();
-#pragma unroll 1
-    for (int g = 0; g < G; ++g) {
-      const size_t base = (size_t(seq) * Hq + kvh * G + g) * a.max_parts;
-      float M = -INFINITY;
-      for (int p0 = 0; p0 < np; p0 += 64) {
-        const int p = p0 + lane;
-        const float mp = p < np ? a.part_ml[2 * (base + p)] : -INFINITY;
-        M = fmaxf(M, wave_max(mp));
-      }
-      float Ls = 0.f;
-      float o[D / 64];
-#pragma unroll
-      for (int i = 0; i < D / 64; ++i) o[i] = 0.f;
-      for (int p0 = 0; p0 < np; p0 += 64) {
-        const int p = p0 + lane;
-        const float wp = p < np ? exp2f(a.part_ml[2 * (base + p)] - M) : 0.f;
-        const float lp = p < np ? a.part_ml[2 * (base + p) + 1] : 0.f;
-        Ls += wave_sum(wp * lp);
-        const int cnt = min(64, np - p0);
-        for (int q = 0; q < cnt; ++q) {
-          const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wp), q));
-          const float* src = a.part_acc + (base + p0 + q) * D;
-#pragma unroll
-          for (int i = 0; i < D / 64; ++i) o[i] = fmaf(wq, src[lane + 64 * i], o[i]);
+          for (int j = 0; j < C::VLB; ++j) a.part_acc[base * D + j * C::DPL + vd] = acc[g][j];
         }
       }
-      const float inv = 1.f / Ls;
-      const size_t ob = (size_t(seq) * Hq + kvh * G + g) * D;
-#pragma unroll
-      for (int i = 0; i < D / 64; ++i) {
-        const float r = o[i] * inv;
-        if constexpr (C::F32) static_cast<float*>(a.out)[ob + lane + 64 * i] = r;
-        else static_cast<uint16_t*>(a.out)[ob + lane + 64 * i] = uint16_t(pack_bf16x2(r, 0.f) & 0xFFFFu);
-      }
     }
-    if (lane == 0) atomicExch(ctr, 0);
   }
 
   // ---- the last wave to leave resets the queue for the next call
@@ -423,6 +407,52 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       atomicExch(&a.counters[0], 0);
       atomicExch(&a.counters[1], 0);
     }
+  }
+}
+
+// Merge of the partitions of multi-partition sequences: one wave per
+// (sequence, query head); out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p.
+template <int D, bool F32OUT>
+__global__ void __launch_bounds__(256) decode_reduce_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int Hq = a.num_q_heads;
+  if (pair >= a.num_seqs * Hq) return;
+  const int seq = pair / Hq, head = pair - seq * Hq;
+  const int L = max(0, a.context_lens[seq]);
+  const int np = max(1, (L + a.part_tokens - 1) / a.part_tokens);
+  if (np == 1) return;                                   // written by the partition kernel
+  const size_t base = size_t(pair) * a.max_parts;
+  float M = -INFINITY;
+  for (int p0 = 0; p0 < np; p0 += 64) {
+    const int p = p0 + lane;
+    const float mp = p < np ? a.part_ml[2 * (base + p)] : -INFINITY;
+    M = fmaxf(M, wave_max(mp));
+  }
+  float Ls = 0.f;
+  float o[D / 64];
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) o[i] = 0.f;
+  for (int p0 = 0; p0 < np; p0 += 64) {
+    const int p = p0 + lane;
+    const float wp = p < np ? exp2f(a.part_ml[2 * (base + p)] - M) : 0.f;
+    const float lp = p < np ? a.part_ml[2 * (base + p) + 1] : 0.f;
+    Ls += wave_sum(wp * lp);
+    const int cnt = min(64, np - p0);
+    for (int q = 0; q < cnt; ++q) {
+      const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wp), q));
+      const float* src = a.part_acc + (base + p0 + q) * D;
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) o[i] = fmaf(wq, src[lane + 64 * i], o[i]);
+    }
+  }
+  const float inv = 1.f / Ls;
+  const size_t ob = size_t(pair) * D;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    const float r = o[i] * inv;
+    if constexpr (F32OUT) static_cast<float*>(a.out)[ob + lane + 64 * i] = r;
+    else static_cast<uint16_t*>(a.out)[ob + lane + 64 * i] = uint16_t(pack_bf16x2(r, 0.f) & 0xFFFFu);
   }
 }
 
@@ -451,6 +481,10 @@ hipError_t launch_decode_t(const DecodeArgs& a0, int64_t upper_items, hipStream_
   DecodeArgs a = a0;
   a.total_waves = int32_t(wgs * 4);
   hipLaunchKernelGGL(kern, dim3(uint32_t(wgs)), dim3(256), lds, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.max_parts <= 1) return e;
+  const int64_t pairs = int64_t(a.num_seqs) * a.num_q_heads;
+  hipLaunchKernelGGL((decode_reduce_kernel<D, KV == KV_F32>), dim3(uint32_t((pairs + 3) / 4)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -115,6 +115,24 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// ---- buffer loads: a descriptor (SGPRs) covering one tile, a 32-bit lane
+// offset and an immediate offset.  Reads past `bytes` return zero.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kBufferDword3 = 0x00020000;   // gfx9 family: 32-bit data format, untyped access
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferDword3);
+}
+__device__ __forceinline__ void buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4& out) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  out = make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2& out) {
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  out = make_uint2(v.x, v.y);
+}
+
 // Order this wave's LDS writes before its following LDS reads by other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

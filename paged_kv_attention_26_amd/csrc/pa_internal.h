@@ -38,7 +38,7 @@ struct DecodeArgs {
   void* out;
   const int32_t* block_table;
   const int32_t* context_lens;
-  int32_t* counters;  // [0] work queue, [1] finished waves, [2..] per (seq, kv head) partitions done
+  int32_t* counters;  // [0] work queue, [1] waves finished (both return to 0 at the end of a call)
   float* part_ml;     // [num_seqs][num_q_heads][max_parts][2]  (running max in log2 units, sum)
   float* part_acc;    // [num_seqs][num_q_heads][max_parts][head_dim]
   float scale_log2;   // softmax scale * log2(e)
