@@ -237,8 +237,25 @@ int pa_prefill_chunk(const pa_kv_cache* cache, const void* q, int32_t q_dtype, v
   if (num_seqs == 0 || max_q_len == 0) return PA_OK;
   if (!q || !out || !cu_q_lens || !seq_lens || !block_table)
     return fail(PA_ERR_NULL, "q / out / cu_q_lens / seq_lens / block_table is NULL");
-  (void)hip_stream;
-  return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk kernel is not built yet");
+  pa::PrefillArgs a{};
+  a.k_cache = cache->k_cache;
+  a.v_cache = cache->v_cache;
+  a.q = q;
+  a.out = out;
+  a.cu_q_lens = cu_q_lens;
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_q_len = max_q_len;
+  hipError_t e = pa::launch_prefill_chunk(a, cache->block_size, G, static_cast<hipStream_t>(hip_stream));
+  if (e == hipErrorInvalidValue) return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for this shape");
+  if (e != hipSuccess) return hip_fail(e, "pa_prefill_chunk launch");
+  g_err[0] = 0;
+  return PA_OK;
 }
 
 }  // extern "C"

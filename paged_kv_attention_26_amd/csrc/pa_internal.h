@@ -46,6 +46,19 @@ struct DecodeArgs {
   int32_t part_tokens, max_parts, total_waves;
 };
 
+struct PrefillArgs {
+  const void* k_cache;
+  const void* v_cache;
+  const void* q;
+  void* out;
+  const int32_t* cu_q_lens;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  float scale_log2;  // softmax scale * log2(e)
+  int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, max_q_len;
+  int32_t num_qtiles, wg_per_pair;  // filled by the launcher
+};
+
 struct DecodeWorkspace {
   size_t counters_off, ml_off, acc_off, total;
 };
@@ -61,5 +74,7 @@ hipError_t launch_copy_blocks(const CopyArgs& a, int num_pairs, hipStream_t s);
 // Returns hipErrorInvalidValue for a combination without a compiled kernel.
 hipError_t launch_decode(const DecodeArgs& a, int kv_kind, int head_dim, int block_size, int group,
                          int64_t upper_items, hipStream_t s);
+// bf16 cache, head_dim 128; hipErrorInvalidValue for an uncompiled combination.
+hipError_t launch_prefill_chunk(const PrefillArgs& a, int block_size, int group, hipStream_t s);
 
 }  // namespace pa

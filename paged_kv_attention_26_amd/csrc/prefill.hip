@@ -1,2 +1,221 @@
-// Chunked-prefill attention (MFMA) -- not built yet.
+// Chunked-prefill attention over a paged prefix on gfx950 matrix cores.
+//
+// What it computes (nanoPD page, "分块预填充": long prompts are cut into
+// chunks interleaved with decode; PD-engineering page 6.1 and serving-stack
+// page 5.2: chunks of a few hundred tokens): sequence j appends a chunk of
+// q_len tokens after P cached tokens; chunk row t, at absolute position
+// P + t, attends to keys 0 .. P + t read through the block table.  Its own
+// K/V were stored by pa_store_kv before the call.
+//
+// How (QK^T and PV are dense contractions, so they run on MFMA; bf16 in,
+// fp32 accumulate):
+//  * A wave owns 32 query rows of one query head; the waves of a workgroup
+//    share a kv head (the G heads of a group, or neighbouring query tiles),
+//    so the K/V tiles they read are shared through the CU's L1.
+//  * Scores are formed transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16
+//    (keys are MFMA rows, queries columns): every lane then owns one query
+//    column, and the softmax statistics and the rescaling of O^T stay in the
+//    lane (one exchange with lane ^ 32 per key tile).
+//  * K rows are loaded into MFMA row m = swap_bits_2_3(key), which makes the
+//    accumulator layout of S^T equal to the B-operand layout of P^T for
+//    O^T = V^T P^T: probabilities go straight from accumulators to bf16
+//    operands, without a pass through LDS.  V is stored transposed per
+//    block, so its A operand (8 consecutive keys of one head dimension) is
+//    one 16-byte load.
+//  * Online softmax in base 2 with the scale folded into exp2's argument;
+//    O^T is rescaled only when some column's running max grows.
+//  * The causal mask is applied only on key tiles that reach the diagonal;
+//    keys past the sequence are masked by select and their V rows zeroed,
+//    so NaN in unused slots never reaches the result.
+//  * Workgroups of one (sequence, kv head) are placed on the same XCD
+//    (workgroup id mod 8), so all query tiles of a sequence share that
+//    XCD's L2 copy of its K/V.
+#include "pa_device.h"
 #include "pa_internal.h"
+
+namespace pa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// MFMA row m of a key tile holds key swap_bits_2_3(m) (an involution).
+__device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+template <int B, int G>
+__global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
+  constexpr int D = 128;
+  constexpr int QT = 32;                 // query rows per wave
+  constexpr int KT = 32;                 // keys per tile
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int hh = lane >> 5;              // lane half: k-slice of operands, row group of accumulators
+  const int n = lane & 31;               // query column / operand row
+  const int Hkv = a.num_kv_heads, Hq = a.num_q_heads;
+
+  // ---- workgroup -> (sequence, kv head, group of 4 column tiles), XCD-aware
+  const int id = blockIdx.x;
+  const int xcd = id & 7;
+  const int k8 = id >> 3;
+  const int pair = (k8 / a.wg_per_pair) * 8 + xcd;
+  if (pair >= a.num_seqs * Hkv) return;
+  const int grp = k8 % a.wg_per_pair;
+  const int seq = pair / Hkv, kvh = pair - seq * Hkv;
+  const int col = grp * 4 + w;
+  const int h_local = col % G;
+  const int qt = a.num_qtiles - 1 - col / G;            // heavy (late) query tiles first
+  if (qt < 0) return;
+  const int q0 = a.cu_q_lens[seq];
+  const int q_len = a.cu_q_lens[seq + 1] - q0;
+  if (qt * QT >= q_len) return;
+  const int total = a.seq_lens[seq];
+  const int P = total - q_len;
+  const int head = kvh * G + h_local;
+  const int t = qt * QT + n;                            // this lane's chunk row
+  const bool valid_q = t < q_len;
+  const int pos = P + t;                                 // absolute position of the query
+  const int key_end = P + min(q_len, (qt + 1) * QT);     // keys the tile's last row needs
+  const int n_tiles = (key_end + KT - 1) / KT;
+  const int* table = a.block_table + size_t(seq) * a.max_blocks_per_seq;
+  const char* kpool = static_cast<const char*>(a.k_cache);
+  const char* vpool = static_cast<const char*>(a.v_cache);
+  const float c = a.scale_log2;
+
+  // ---- Q^T as 8 B operands (k = 16 head dims each): row q0 + t, dims 16s + 8hh .. + 7
+  uint4 qb[8];
+  {
+    const int row = q0 + min(t, q_len - 1);
+    const uint16_t* qr = static_cast<const uint16_t*>(a.q) + (size_t(row) * Hq + head) * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qb[s] = *reinterpret_cast<const uint4*>(qr + 16 * s);
+  }
+
+  f32x16_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32x16_t{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int my_key = swap23(n);                          // key of MFMA row n within a tile
+  const int first_row_pos = P + qt * QT;                 // smallest query position of the tile
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int k0 = kt * KT;
+    // ---- S^T = K Q^T  (A: lane row n = key k0 + my_key, dims 16s + 8hh)
+    uint4 ka[8];
+    {
+      const int key = min(k0 + my_key, key_end - 1);
+      const int blk = table[key / B];
+      const char* kr = kpool + ((size_t(blk) * Hkv + kvh) * B + key % B) * (D * 2) + 16 * hh;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) ka[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
+    }
+    // V^T operands: d-tile dt (dims 32dt + n), key slice ks (keys k0 + 16ks + 8hh .. + 7)
+    uint4 va[4][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int kb = min(k0 + 16 * ks, key_end - 1);
+      const int blk = table[kb / B];
+      const int off = (B == 16 ? 0 : (k0 + 16 * ks) % B) + 8 * hh;
+      const char* vb = vpool + (size_t(blk) * Hkv + kvh) * size_t(D * B * 2) + off * 2;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        va[dt][ks] = *reinterpret_cast<const uint4*>(vb + size_t(32 * dt + n) * (B * 2));
+    }
+    f32x16_t s = f32x16_t{};
+#pragma unroll
+    for (int st = 0; st < 8; ++st) s = mfma32(ka[st], qb[st], s);
+
+    // accumulator r = 4i + j holds MFMA row 8i + 4hh + j, i.e. key k0 + swap23(8i + 4hh + j)
+    if (k0 + KT - 1 > first_row_pos) {                   // tile reaches the diagonal or the end
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + swap23(8 * (r >> 2) + 4 * hh + (r & 3));
+        s[r] = (key <= pos && key < key_end) ? s[r] : -INFINITY;
+      }
+    }
+    float mt = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    if (__any(m_new > m_run)) {
+      const float al = exp2f((m_run - m_new) * c);
+      l_run *= al;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= al;
+      m_run = m_new;
+    }
+    const float mc = m_run * c;
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = exp2f(fmaf(s[r], c, -mc));
+      l_run += p[r];
+    }
+    // P^T operands: key slice ks takes accumulators 8ks .. 8ks + 7 (keys k0 + 16ks + 8hh + 0..7)
+    uint4 pb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      pb[ks] = make_uint4(pack_bf16x2(p[8 * ks + 0], p[8 * ks + 1]), pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]),
+                          pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]), pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7]));
+    if (k0 + KT > key_end) {                              // zero V rows of keys past the end (NaN poison)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int kb = k0 + 16 * ks + 8 * hh;
+        uint32_t msk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          msk[e] = (kb + 2 * e < key_end ? 0x0000FFFFu : 0u) | (kb + 2 * e + 1 < key_end ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          va[dt][ks].x &= msk[0]; va[dt][ks].y &= msk[1]; va[dt][ks].z &= msk[2]; va[dt][ks].w &= msk[3];
+        }
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      o[dt] = mfma32(va[dt][0], pb[0], o[dt]);
+      o[dt] = mfma32(va[dt][1], pb[1], o[dt]);
+    }
+  }
+
+  // ---- normalise and store: accumulator r of d-tile dt is dim 32dt + 8(r/4) + 4hh + (r%4)
+  const float l = l_run + __shfl_xor(l_run, 32);
+  if (!valid_q) return;
+  const float inv = 1.f / l;
+  uint16_t* orow = static_cast<uint16_t*>(a.out) + (size_t(q0 + t) * Hq + head) * D + 4 * hh;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * i;
+      *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * i) =
+          make_uint2(pack_bf16x2(o[dt][r] * inv, o[dt][r + 1] * inv), pack_bf16x2(o[dt][r + 2] * inv, o[dt][r + 3] * inv));
+    }
+}
+
+hipError_t launch_prefill_chunk(const PrefillArgs& a0, int block_size, int group, hipStream_t s) {
+  PrefillArgs a = a0;
+  a.num_qtiles = (a.max_q_len + 31) / 32;
+  a.wg_per_pair = (group * a.num_qtiles + 3) / 4;
+  const int64_t pairs = int64_t(a.num_seqs) * a.num_kv_heads;
+  const int64_t wgs = ((pairs + 7) / 8) * 8 * a.wg_per_pair;
+  if (wgs == 0) return hipSuccess;
+  if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+#define PA_PF(b, g) \
+  if (block_size == b && group == g) { \
+    hipLaunchKernelGGL((prefill_kernel<b, g>), dim3(uint32_t(wgs)), dim3(256), 0, s, a); \
+    return hipGetLastError(); \
+  }
+  PA_PF(16, 1) PA_PF(16, 2) PA_PF(16, 4) PA_PF(16, 8)
+  PA_PF(32, 1) PA_PF(32, 2) PA_PF(32, 4) PA_PF(32, 8)
+#undef PA_PF
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

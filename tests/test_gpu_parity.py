@@ -203,3 +203,80 @@ def test_fp8_codes_round_trip_through_store_and_decode():
     got = out.float().cpu().numpy().astype(np.float64)              # [1, 8, 128]
     want = np.repeat(row.astype(np.float64), 4, axis=1)             # kv head h -> q heads 4h..4h+3
     assert np.array_equal(got[0], want[0])
+
+
+# ------------------------------------------------------------ chunked prefill
+def chunk_batch(name, P, q, B=16, Hq=32, Hkv=8, seed=41):
+    rng = np.random.default_rng(seed)
+    n = len(P)
+    return W.paged_batch(name, seed, kv_dtype="bf16", io_dtype="bf16", Hq=Hq, Hkv=Hkv, d=128, B=B,
+                         prior_lens=P, new_lens=q, is_chunk=np.ones(n, bool), rng=rng)
+
+
+CHUNKS = {
+    "c4s": lambda: W.config4(small=True),
+    "prefix0": lambda: chunk_batch("prefix0", [0, 0], [37, 64]),
+    "ragged": lambda: chunk_batch("ragged", [5, 100, 33, 512, 0], [1, 31, 33, 97, 129]),
+    "ragged-b32": lambda: chunk_batch("ragged-b32", [5, 100, 33, 512, 0], [1, 31, 33, 97, 129], B=32),
+    "g1": lambda: chunk_batch("g1", [17, 300], [45, 70], Hq=8, Hkv=8),
+    "g2": lambda: chunk_batch("g2", [17, 300], [45, 70], Hq=16, Hkv=8),
+    "g8": lambda: chunk_batch("g8", [17, 300], [45, 70], Hq=32, Hkv=4),
+}
+
+
+@pytest.mark.parametrize("name", list(CHUNKS))
+def test_prefill_chunk_matches_oracle(name):
+    from paged_kv_attention_26_amd import runner
+    say(f"[gpu] prefill {name}")
+    batch = CHUNKS[name]()
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    out = runner.chunk_step(g)
+    torch.cuda.synchronize()
+    st = OS.build(batch)
+    ref = OS.chunk_ref(batch, st)
+    got = out_f64(out)
+    assert np.all(np.isfinite(got))
+    err = np.max(np.abs(got - ref))
+    say(f"      max abs err {err:.3e}")
+    assert err < TOL["bf16"]
+    if (~batch.is_chunk).any():                      # the mixed batch's decode half too
+        dref = OS.decode_ref(batch, st)
+        derr = np.max(np.abs(out_f64(runner.decode_step(g)) - dref))
+        say(f"      decode max abs err {derr:.3e}")
+        assert derr < TOL["bf16"]
+
+
+def test_prefill_chunk_of_one_row_matches_decode():
+    from paged_kv_attention_26_amd import binding as pa, runner
+    batch = chunk_batch("one-row", [0, 1, 15, 16, 200, 511], [1, 1, 1, 1, 1, 1])
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    pre = out_f64(runner.chunk_step(g))
+    c = g.chunk
+    dec = out_f64(pa.decode(g.cache, c["q"], c["table"], c["seq_lens"], c["max_seq"], batch.scale))
+    assert np.max(np.abs(pre - dec)) < 1e-2
+
+
+def test_prefill_full_mixed_batch_sampled():
+    """The full mixed chunked-prefill batch (8 chunks of 512 on prefixes up to
+    7680, 64 decodes): every output of two chunk sequences against the oracle."""
+    from paged_kv_attention_26_amd import runner
+    say("[gpu] prefill full mixed batch")
+    batch = W.config4()
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    out = out_f64(runner.chunk_step(g))
+    torch.cuda.synchronize()
+    st = OS.build(batch)
+    ch = np.flatnonzero(batch.is_chunk)
+    cu = np.concatenate([[0], np.cumsum(batch.new_lens[ch])])
+    from oracle import paged
+    for j in (0, len(ch) - 1):
+        i = ch[j]
+        tab = OS.table_array([st.tables[i]], st.pad_block)
+        ref = paged.prefill_chunk_attention(st.kc, st.vc, "bf16", batch.q_chunk[cu[j]:cu[j + 1]], "bf16",
+                                            [0, int(batch.new_lens[i])], [int(batch.total_lens[i])], tab, batch.scale)
+        err = np.max(np.abs(out[cu[j]:cu[j + 1]] - ref))
+        say(f"      seq {j} (prefix {int(batch.prior_lens[i])}) max abs err {err:.3e}")
+        assert err < TOL["bf16"]
