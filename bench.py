@@ -66,8 +66,8 @@ def extras(pa, runner, W, torch):
         b = W.config3(B)
         g = runner.prepare(b)
         runner.store_step(g)
-        ws = pa.decode_workspace(len(g.dec["idx"]), b.num_q_heads, b.head_dim, g.dec["max_len"], 512)
-        med, p10, p90 = timed_calls(lambda: runner.decode_step(g, partition_tokens=512, workspace=ws), 20)
+        ws = pa.decode_workspace(len(g.dec["idx"]), b.num_q_heads, b.head_dim, g.dec["max_len"], 0)
+        med, p10, p90 = timed_calls(lambda: runner.decode_step(g, partition_tokens=0, workspace=ws), 20)
         byt = kv_bytes(g.dec["host_lens"], b.num_kv_heads, b.head_dim, 2)
         out[f"long_context_decode_b{B}"] = dict(GBps=round(byt / med / 1e6, 1), ms=round(med, 4),
                                                 p10_ms=round(p10, 4), p90_ms=round(p90, 4),
@@ -201,7 +201,7 @@ def main():
                                "bf16 KV, block 16, store 32 tokens + paged decode",
                    "global_batch": int(len(lens_all)), "seq_len": int(np.max(lens_all)),
                    "kv_tokens": int(np.sum(lens_all)), "layer_caches": args.layers,
-                   "partition_tokens": args.partition or 512, "parallelism": "single-gpu"},
+                   "partition_tokens": args.partition or 64, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "pa::decode_kernel<bf16, d128, B16, G4>",

@@ -111,9 +111,10 @@ int pa_store_kv(const pa_kv_cache* cache, const void* k_new, const void* v_new, 
 int pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src_dst, int32_t num_pairs,
                    void* hip_stream);
 
-/* Bytes of device workspace pa_decode needs for these sizes (host call, no
- * HIP).  partition_tokens as for pa_decode (0 = the default, 512).  Returns
- * 0 for invalid sizes. */
+/* Bytes of device workspace pa_decode needs (host call, no HIP): two partial
+ * results per wavefront for at most 4096 wavefronts and 8 query heads per kv
+ * head, about 34 MB at head_dim 128 whatever the batch.  partition_tokens as
+ * for pa_decode.  Returns 0 for invalid sizes. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_tokens);
 
@@ -129,22 +130,24 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                  just stored.  A length of 0 gives an output of 0.
  *   max_context_len : host upper bound of context_lens (sizes the launch).
  *   out[s][h] = sum_i softmax_i(scale * <q[s][h], k_i>) * v_i over tokens
- *   i < context_lens[s], accumulated in fp32.
+ *   i < context_lens[s], accumulated in fp32.  scale must be finite and > 0
+ *   (the softmax scale, 1/sqrt(head_dim) for the pages' attention).
  *
- * Long contexts are split into partitions of partition_tokens tokens
- * (0 = 512; otherwise a multiple of 64 and at most 64 * block_size); each
- * partition keeps a running max / sum and the partitions are merged by
- * log-sum-exp rescaling.  The result does not depend on partition_tokens
- * beyond fp32 rounding.
+ * Work is cut into partitions of partition_tokens tokens of one (sequence,
+ * kv head) (0 = 64; otherwise a multiple of 64 and at most 64 * block_size).
+ * Every wavefront of the launch takes an equal, contiguous run of
+ * partitions and keeps a running max / sum across the partitions of one
+ * (sequence, kv head); where runs cut a (sequence, kv head) apart, their
+ * partial results are merged by log-sum-exp rescaling in a second kernel.
+ * The result does not depend on partition_tokens or on the split beyond
+ * fp32 rounding.
  *
  * dtypes: F32 cache -> q, out F32; BF16 cache -> q, out BF16;
  * FP8 cache -> q, out BF16.
  *
- * workspace: device memory of at least pa_decode_workspace_bytes() bytes.
- * It must be zero-filled before its first use; every call leaves its
- * counters zero again when it completes, so one workspace serves any number
- * of successive calls on one stream.  Two calls that may run at the same
- * time must not share a workspace. */
+ * workspace: device memory of at least pa_decode_workspace_bytes() bytes
+ * (scratch for the partial results; no initial contents needed).  Two calls
+ * that may run at the same time must not share a workspace. */
 int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
               int32_t num_seqs, int32_t num_q_heads, float scale, const int32_t* block_table,
               int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
@@ -162,6 +165,7 @@ int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* ou
  *   seq_lens  : [num_seqs] int32, tokens of the sequence including the chunk
  *   block_table : [num_seqs][max_blocks_per_seq] int32
  *   max_q_len, max_seq_len : host upper bounds (size the launch)
+ * scale must be finite and > 0.
  * QK^T and PV run on bf16 matrix cores with fp32 accumulation; the
  * probabilities are rounded to bf16 for PV.  Supported: BF16 cache,
  * head_dim 128. */

@@ -109,9 +109,9 @@ def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, par
 
 def decode_workspace(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens=0,
                      device="cuda") -> torch.Tensor:
-    """Zero-filled workspace (pa_decode leaves it zeroed again after each call)."""
+    """Scratch for pa_decode's partial results (no initial contents needed)."""
     n = decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens)
-    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def decode(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor, context_lens: torch.Tensor,

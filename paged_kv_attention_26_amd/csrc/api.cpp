@@ -33,7 +33,7 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr int kDefaultPartition = 512;
+constexpr int kDefaultPartition = 64;
 constexpr int kMaxSeqs = 8192;  // the decode kernel keeps a prefix over sequences in LDS
 
 int elem_bytes(int dt) { return dt == PA_F32 ? 4 : dt == PA_BF16 ? 2 : 1; }
@@ -68,11 +68,6 @@ int resolve_partition(int32_t p, int32_t block_size, int32_t* out) {
   return PA_OK;
 }
 
-size_t workspace_bytes(int64_t S, int64_t Hq, int64_t D, int64_t max_ctx, int64_t P) {
-  const int64_t max_parts = max_ctx > 0 ? (max_ctx + P - 1) / P : 1;
-  return pa::decode_workspace_layout(S, Hq, D, max_parts).total;
-}
-
 }  // namespace
 
 namespace pa {
@@ -85,13 +80,13 @@ int set_error(int code, const char* fmt, ...) {
   return code;
 }
 
-DecodeWorkspace decode_workspace_layout(int64_t S, int64_t Hq, int64_t D, int64_t max_parts) {
+DecodeWorkspace decode_workspace_layout(int64_t D) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t slots = size_t(kDecodeMaxWaves) * 2 * kDecodeMaxGroup;   // two partials per wave
   DecodeWorkspace w;
-  w.counters_off = 0;
-  w.ml_off = up(2 * sizeof(int32_t));
-  w.acc_off = w.ml_off + up(size_t(S * Hq * max_parts * 2) * sizeof(float));
-  w.total = w.acc_off + up(size_t(S * Hq * max_parts * D) * sizeof(float));
+  w.ml_off = 0;
+  w.acc_off = up(slots * 2 * sizeof(float));
+  w.total = w.acc_off + up(slots * size_t(D) * sizeof(float));
   return w;
 }
 
@@ -148,7 +143,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
   int32_t P = partition_tokens == 0 ? kDefaultPartition : partition_tokens;
   if (P < 64 || P % 64) return 0;
-  return workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, P);
+  return pa::decode_workspace_layout(head_dim).total;
 }
 
 int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
@@ -171,15 +166,14 @@ int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* ou
   if (max_blocks_per_seq < need_blocks || max_blocks_per_seq <= 0)
     return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d < %lld blocks of max_context_len", max_blocks_per_seq,
                 (long long)need_blocks);
-  if (!(std::isfinite(scale))) return fail(PA_ERR_SHAPE, "scale is not finite");
+  if (!(std::isfinite(scale)) || !(scale > 0.f)) return fail(PA_ERR_SHAPE, "scale must be finite and > 0");
   int32_t P = 0;
   rc = resolve_partition(partition_tokens, cache->block_size, &P);
   if (rc) return rc;
   if (num_seqs == 0) return PA_OK;
   if (!q || !out || !block_table || !context_lens || !workspace)
     return fail(PA_ERR_NULL, "q / out / block_table / context_lens / workspace is NULL");
-  const int64_t max_parts = max_context_len > 0 ? (int64_t(max_context_len) + P - 1) / P : 1;
-  const pa::DecodeWorkspace lay = pa::decode_workspace_layout(num_seqs, num_q_heads, cache->head_dim, max_parts);
+  const pa::DecodeWorkspace lay = pa::decode_workspace_layout(cache->head_dim);
   if (workspace_bytes_given < lay.total)
     return fail(PA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes_given, lay.total);
   char* ws = static_cast<char*>(workspace);
@@ -192,7 +186,6 @@ int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* ou
   a.out = out;
   a.block_table = block_table;
   a.context_lens = context_lens;
-  a.counters = reinterpret_cast<int32_t*>(ws + lay.counters_off);
   a.part_ml = reinterpret_cast<float*>(ws + lay.ml_off);
   a.part_acc = reinterpret_cast<float*>(ws + lay.acc_off);
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -201,10 +194,10 @@ int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* ou
   a.num_kv_heads = cache->num_kv_heads;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.part_tokens = P;
-  a.max_parts = int32_t(max_parts);
   const int kv = cache->dtype == PA_F32 ? pa::KV_F32 : cache->dtype == PA_BF16 ? pa::KV_BF16 : pa::KV_FP8;
-  const int64_t upper_items = int64_t(num_seqs) * cache->num_kv_heads * max_parts;
-  hipError_t e = pa::launch_decode(a, kv, cache->head_dim, cache->block_size, G, upper_items,
+  const int64_t max_parts = max_context_len > 0 ? (int64_t(max_context_len) + P - 1) / P : 1;
+  const int64_t upper_units = int64_t(num_seqs) * cache->num_kv_heads * max_parts;
+  hipError_t e = pa::launch_decode(a, kv, cache->head_dim, cache->block_size, G, upper_units,
                                    static_cast<hipStream_t>(hip_stream));
   if (e == hipErrorInvalidValue) return fail(PA_ERR_UNSUPPORTED, "no decode kernel for this shape");
   if (e != hipSuccess) return hip_fail(e, "pa_decode launch");
@@ -233,7 +226,7 @@ int pa_prefill_chunk(const pa_kv_cache* cache, const void* q, int32_t q_dtype, v
   if (max_blocks_per_seq < need_blocks || max_blocks_per_seq <= 0)
     return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d < %lld blocks of max_seq_len", max_blocks_per_seq,
                 (long long)need_blocks);
-  if (!(std::isfinite(scale))) return fail(PA_ERR_SHAPE, "scale is not finite");
+  if (!(std::isfinite(scale)) || !(scale > 0.f)) return fail(PA_ERR_SHAPE, "scale must be finite and > 0");
   if (num_seqs == 0 || max_q_len == 0) return PA_OK;
   if (!q || !out || !cu_q_lens || !seq_lens || !block_table)
     return fail(PA_ERR_NULL, "q / out / cu_q_lens / seq_lens / block_table is NULL");

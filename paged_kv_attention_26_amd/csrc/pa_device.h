@@ -124,12 +124,14 @@ constexpr int kBufferDword3 = 0x00020000;   // gfx9 family: 32-bit data format, 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferDword3);
 }
-__device__ __forceinline__ void buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4& out) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+// voff: the lane's offset (VGPR); soff: a wave-uniform constant offset,
+// which the compiler folds into the instruction's immediate field.
+__device__ __forceinline__ void buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint4& out) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
   out = make_uint4(v.x, v.y, v.z, v.w);
 }
-__device__ __forceinline__ void buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2& out) {
-  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+__device__ __forceinline__ void buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint2& out) {
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
   out = make_uint2(v.x, v.y);
 }
 

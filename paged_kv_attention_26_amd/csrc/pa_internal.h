@@ -38,13 +38,16 @@ struct DecodeArgs {
   void* out;
   const int32_t* block_table;
   const int32_t* context_lens;
-  int32_t* counters;  // [0] work queue, [1] waves finished (both return to 0 at the end of a call)
-  float* part_ml;     // [num_seqs][num_q_heads][max_parts][2]  (running max in log2 units, sum)
-  float* part_acc;    // [num_seqs][num_q_heads][max_parts][head_dim]
+  float* part_ml;     // [total_waves][2][G][2]  (running max in log2 units, sum) of split items
+  float* part_acc;    // [total_waves][2][G][head_dim]
   float scale_log2;   // softmax scale * log2(e)
   int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq;
-  int32_t part_tokens, max_parts, total_waves;
+  int32_t part_tokens, total_waves;  // total_waves is set by the launcher
 };
+
+// Upper bound on the waves one decode launch uses (the workspace is sized for it).
+constexpr int kDecodeMaxWaves = 4096;
+constexpr int kDecodeMaxGroup = 8;
 
 struct PrefillArgs {
   const void* k_cache;
@@ -60,20 +63,19 @@ struct PrefillArgs {
 };
 
 struct DecodeWorkspace {
-  size_t counters_off, ml_off, acc_off, total;
+  size_t ml_off, acc_off, total;
 };
 
 // Record the message of a failed call for pa_last_error(); returns code.
 int set_error(int code, const char* fmt, ...);
 
-DecodeWorkspace decode_workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,
-                                        int64_t max_parts);
+DecodeWorkspace decode_workspace_layout(int64_t head_dim);
 
 hipError_t launch_store_kv(const StoreArgs& a, int kv_kind, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyArgs& a, int num_pairs, hipStream_t s);
 // Returns hipErrorInvalidValue for a combination without a compiled kernel.
 hipError_t launch_decode(const DecodeArgs& a, int kv_kind, int head_dim, int block_size, int group,
-                         int64_t upper_items, hipStream_t s);
+                         int64_t upper_units, hipStream_t s);
 // bf16 cache, head_dim 128; hipErrorInvalidValue for an uncompiled combination.
 hipError_t launch_prefill_chunk(const PrefillArgs& a, int block_size, int group, hipStream_t s);
 

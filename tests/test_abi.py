@@ -73,6 +73,8 @@ def decode_call(c, **kw):
     (dict(c=cache(), lens=None), L.PA_ERR_NULL),
     (dict(c=cache(), S=-1), L.PA_ERR_SHAPE),
     (dict(c=cache(), scale=float("nan")), L.PA_ERR_SHAPE),
+    (dict(c=cache(), scale=0.0), L.PA_ERR_SHAPE),
+    (dict(c=cache(), scale=-0.125), L.PA_ERR_SHAPE),
 ])
 def test_decode_rejects_bad_arguments(kw, code):
     c = kw.pop("c")
@@ -113,14 +115,17 @@ def test_prefill_rejects_bad_arguments():
 
 
 def test_workspace_size_query():
+    """The workspace holds two partial results (m, l and an fp32 accumulator
+    per query head of a group of at most 8) for each of at most 4096 waves,
+    whatever the batch or context length."""
     lib = L.lib()
     a = lib.pa_decode_workspace_bytes(32, 32, 128, 4096, 512)
-    b = lib.pa_decode_workspace_bytes(32, 32, 128, 8192, 512)
-    assert 0 < a < b
+    b = lib.pa_decode_workspace_bytes(32, 32, 128, 131072, 64)
+    assert a == b > 0
+    assert a >= 4096 * 2 * 8 * (128 + 2) * 4
+    assert lib.pa_decode_workspace_bytes(32, 32, 64, 4096, 512) < a
     assert lib.pa_decode_workspace_bytes(-1, 32, 128, 4096, 512) == 0
     assert lib.pa_decode_workspace_bytes(32, 32, 128, 4096, 100) == 0
-    # m, l and an fp32 accumulator per (sequence, head, partition) fit
-    assert a >= 32 * 32 * 8 * (128 + 2) * 4
 
 
 # ------------------------------------------- native block manager == oracle

@@ -61,6 +61,17 @@ def edge_batch(kv="bf16", B=16):
                          prior_lens=prior, new_lens=new, is_chunk=np.zeros(len(lens), bool), rng=rng)
 
 
+def skew_batch():
+    """One long sequence beside empty and one-token ones: far fewer work units
+    than the host's upper bound, so the launch has more waves than units."""
+    rng = np.random.default_rng(78)
+    lens = np.array([6000] + [0] * 8 + [1] * 7)
+    prior = np.maximum(lens - 1, 0)
+    new = (lens > 0).astype(np.int64)
+    return W.paged_batch("skew-bf16", 78, kv_dtype="bf16", io_dtype="bf16", Hq=32, Hkv=8, d=128, B=16,
+                         prior_lens=prior, new_lens=new, is_chunk=np.zeros(len(lens), bool), rng=rng)
+
+
 SMALL = {
     "c1": lambda: W.config1(),
     "c2s": lambda: W.config2(small=True),
@@ -69,6 +80,7 @@ SMALL = {
     "edge16": lambda: edge_batch("bf16", 16),
     "edge32": lambda: edge_batch("bf16", 32),
     "edge-f32": lambda: edge_batch("f32", 16),
+    "skew": skew_batch,
 }
 
 
@@ -105,8 +117,7 @@ def test_decode_matches_oracle(name, part):
 
 
 def test_decode_repeated_calls_reuse_the_workspace():
-    """The workspace counters reset themselves: back-to-back calls on one
-    workspace give bit-identical results."""
+    """Back-to-back calls on one workspace give bit-identical results."""
     from paged_kv_attention_26_amd import binding as pa, runner
     batch = W.config3(16, small=True)
     g = runner.prepare(batch)
@@ -117,7 +128,6 @@ def test_decode_repeated_calls_reuse_the_workspace():
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
-    assert int(ws[:8].view(torch.int32).abs().sum()) == 0
 
 
 def test_block_permutation_leaves_output_bit_identical():
