@@ -27,6 +27,30 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6
 
 
+# HBM bytes per decode_kernel launch on this workload, from rocprofv3 FETCH_SIZE
+# and WRITE_SIZE passes scaled by the same counters on a plain 1 GiB copy
+# (bench.py --copy-probe 1024), and the hash of the kernel sources they were
+# taken on: once those sources change the figure no longer applies.
+DECODE_TRAFFIC = {"sources_sha256": "36a5e72b0b2ad70b04c61646985270e272dde0d92645dcb8762b6b64aee2ddc2",
+                  "bytes_per_launch": 312474325}
+DECODE_SOURCES = ("decode_kernel.h", "pa_device.h", "pa_internal.h", "decode_bf16.hip")
+
+
+def decode_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_attention_26_amd", "csrc")
+    for name in DECODE_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def decode_traffic():
+    ok = DECODE_TRAFFIC["sources_sha256"] == decode_sources_sha256()
+    return DECODE_TRAFFIC["bytes_per_launch"] if ok else None
+
+
 def kv_bytes(lens, hkv, d, es):
     return int(np.sum(lens)) * 2 * hkv * d * es
 
@@ -40,6 +64,8 @@ def parse():
     ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = library default)")
     ap.add_argument("--no-extras", action="store_true", help="skip the secondary measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB device buffer 4 times (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
@@ -143,6 +169,17 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_probe:
+        # A plain device-to-device copy of known size: each launch reads and
+        # writes exactly MIB MiB, the yardstick for FETCH_SIZE / WRITE_SIZE.
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_per_launch": n, "launches": 4}), flush=True)
+        return
     import workloads as W
     from paged_kv_attention_26_amd import binding as pa, runner
 
@@ -203,7 +240,7 @@ def main():
                    "kv_tokens": int(np.sum(lens_all)), "layer_caches": args.layers,
                    "partition_tokens": args.partition or 64, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": decode_traffic(),
                      "kernel": "pa::decode_kernel<bf16, d128, B16, G4>",
                      "kernel_ms_avg": round(dec_avg, 5), "kernel_ms_median": round(float(np.median(dec_ms)), 5),
                      "algorithmic_bytes_per_launch": step_bytes},
