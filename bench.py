@@ -31,8 +31,8 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6
 # and WRITE_SIZE passes scaled by the same counters on a plain 1 GiB copy
 # (bench.py --copy-probe 1024), and the hash of the kernel sources they were
 # taken on: once those sources change the figure no longer applies.
-DECODE_TRAFFIC = {"sources_sha256": "36a5e72b0b2ad70b04c61646985270e272dde0d92645dcb8762b6b64aee2ddc2",
-                  "bytes_per_launch": 312474325}
+DECODE_TRAFFIC = {"sources_sha256": "a7efe010b6e4c39ce663d825e04c611ceafa16c19ccaad8bbc2c148ea33f6a2a",
+                  "bytes_per_launch": 317108591}
 DECODE_SOURCES = ("decode_kernel.h", "pa_device.h", "pa_internal.h", "decode_bf16.hip")
 
 

@@ -138,7 +138,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * Every wavefront of the launch takes an equal, contiguous run of
  * partitions and keeps a running max / sum across the partitions of one
  * (sequence, kv head); where runs cut a (sequence, kv head) apart, their
- * partial results are merged by log-sum-exp rescaling in a second kernel.
+ * partial results are merged by log-sum-exp rescaling, in the same kernel,
+ * by whichever of those wavefronts finishes last.
  * The result does not depend on partition_tokens or on the split beyond
  * fp32 rounding.
  *
@@ -146,8 +147,11 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * FP8 cache -> q, out BF16.
  *
  * workspace: device memory of at least pa_decode_workspace_bytes() bytes
- * (scratch for the partial results; no initial contents needed).  Two calls
- * that may run at the same time must not share a workspace. */
+ * holding partial results and one arrival counter per split item.  It must
+ * be zero-filled before its first use (hipMemset once); every completed call
+ * leaves the counters at zero again, so the same workspace serves any number
+ * of later calls, of any shape, on one stream.  Two calls that may run at
+ * the same time must not share a workspace. */
 int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
               int32_t num_seqs, int32_t num_q_heads, float scale, const int32_t* block_table,
               int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,

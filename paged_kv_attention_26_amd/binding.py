@@ -109,9 +109,25 @@ def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, par
 
 def decode_workspace(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens=0,
                      device="cuda") -> torch.Tensor:
-    """Scratch for pa_decode's partial results (no initial contents needed)."""
+    """Workspace for pa_decode: partial results and per-item arrival counters.
+    It is zero-filled here, once; every pa_decode call leaves it ready for the
+    next.  Calls that may run at the same time need workspaces of their own."""
     n = decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+_default_workspaces = {}
+
+
+def _default_workspace(head_dim, device, stream_handle) -> torch.Tensor:
+    """One zero-filled workspace per (device, stream, head_dim), kept for the
+    process: calls on one stream run one after another, so they may share it."""
+    key = (torch.device(device).index, stream_handle, int(head_dim))
+    ws = _default_workspaces.get(key)
+    if ws is None:
+        ws = decode_workspace(1, 1, head_dim, 1, 0, device=device)
+        _default_workspaces[key] = ws
+    return ws
 
 
 def decode(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor, context_lens: torch.Tensor,
@@ -123,7 +139,7 @@ def decode(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor, context_l
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
-        workspace = decode_workspace(S, Hq, D, max_context_len, partition_tokens, device=q.device)
+        workspace = _default_workspace(D, q.device, _stream(stream).value)
     if block_table.dim() != 2 or block_table.shape[0] != S or context_lens.numel() != S:
         raise ValueError("block_table must be [S, max_blocks] and context_lens [S]")
     io = DTYPE_CODES["f32"] if cache.dtype == "f32" else DTYPE_CODES["bf16"]

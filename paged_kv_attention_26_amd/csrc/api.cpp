@@ -84,8 +84,9 @@ DecodeWorkspace decode_workspace_layout(int64_t D) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t slots = size_t(kDecodeMaxWaves) * 2 * kDecodeMaxGroup;   // two partials per wave
   DecodeWorkspace w;
-  w.ml_off = 0;
-  w.acc_off = up(slots * 2 * sizeof(float));
+  w.arrivals_off = 0;
+  w.ml_off = up(size_t(kDecodeMaxWaves) * sizeof(int32_t));
+  w.acc_off = w.ml_off + up(slots * 2 * sizeof(float));
   w.total = w.acc_off + up(slots * size_t(D) * sizeof(float));
   return w;
 }
@@ -186,6 +187,7 @@ int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* ou
   a.out = out;
   a.block_table = block_table;
   a.context_lens = context_lens;
+  a.arrivals = reinterpret_cast<int32_t*>(ws + lay.arrivals_off);
   a.part_ml = reinterpret_cast<float*>(ws + lay.ml_off);
   a.part_acc = reinterpret_cast<float*>(ws + lay.acc_off);
   a.scale_log2 = scale * 1.4426950408889634f;

@@ -18,14 +18,18 @@
 //  * A (sequence, kv head) whose units all fall in one wave's range is
 //    written out directly.  Otherwise each wave that touched it writes a
 //    partial (max, sum, acc) -- at most two per wave, for the first and the
-//    last item of its range -- and a small reduce kernel merges them by
-//    log-sum-exp rescaling.
-//  * Block ids are fetched one 64-token step ahead of their use; every K/V
-//    load is a raw buffer load of one (block, kv head) tile (a descriptor,
-//    one lane offset, immediate offsets), 16 bytes per lane (8 for fp8).
+//    last item of its range.  After its whole range a wave counts itself in
+//    on those items; the last of an item's waves to arrive merges the
+//    partials by log-sum-exp rescaling, in the same launch.
+//  * A scalar cursor walks the steps of the range across items: block ids
+//    are fetched one 64-token step ahead of their use, and every K/V load is
+//    a raw buffer load of one (block, kv head) tile (a descriptor, one lane
+//    offset, immediate offsets), 16 bytes per lane (8 for fp8).
 //  * Loads are software-pipelined: the next step's K tile is issued right
 //    after this step's scores, its V tile right after this step's PV, so a
-//    wave keeps one step of K and V in flight while it computes.
+//    wave keeps one step of K and V in flight while it computes -- also from
+//    the last step of one item into the first of the next, whose query is
+//    fetched along with them.
 //  * QK^T: a key row is spread over LPR lanes; each lane forms partial dot
 //    products for the G heads with v_dot2_f32_bf16 (fp32 FMA for fp32
 //    caches).  The G partials are reduced by a transpose-reduce inside
@@ -131,6 +135,98 @@ __device__ __forceinline__ int find_seq(const int* s_prefix, int S, int key) {
   return uniform(lo);
 }
 
+// Cross-wave hand-off of split items.  Partials and arrival counters are only
+// ever touched through agent-scope atomics, which the L2 of one XCD does not
+// hold back from the other XCDs.  A wave waits until its partial stores have
+// completed (vmcnt(0)) before it counts itself in, and the last wave to arrive
+// reads the partials only after its counter increment has returned, so no
+// cache write-back or invalidation is needed.
+__device__ __forceinline__ void xstore(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float xload(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Count this wave in on up to two split items (counter c[i], n[i] waves
+// each); last[i] is true for the last of an item's waves to arrive, which then
+// owns its merge and leaves the counter at zero for the next call.  Both
+// increments go out before either result is awaited.
+__device__ __forceinline__ void arrive_last2(int32_t* c0, int n0, bool h0, int32_t* c1, int n1, bool h1,
+                                             bool& last0, bool& last1) {
+  int r0 = 0, r1 = 0;
+  const bool l0 = (threadIdx.x & 63) == 0;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);                      // this wave's partial stores are complete
+  __builtin_amdgcn_sched_barrier(0);
+  if (l0 && h0) r0 = __hip_atomic_fetch_add(c0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (l0 && h1) r1 = __hip_atomic_fetch_add(c1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  r1 = __builtin_amdgcn_readfirstlane(r1);
+  last0 = h0 && r0 == n0 - 1;
+  last1 = h1 && r1 == n1 - 1;
+  if (l0 && last0) __hip_atomic_store(c0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (l0 && last1) __hip_atomic_store(c1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge of the n partials of one (sequence, kv head) split over waves
+// w0 .. w0 + n - 1: out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i
+// (m in log2 units).  Wave w0 holds the item in slot 0 if the item opens its
+// range, else in slot 1; every later wave holds it in slot 0.
+template <int D, int G, bool F32OUT>
+__device__ __forceinline__ void merge_split(const DecodeArgs& a, int seq, int kvh, int w0, int n, bool w0_first) {
+  constexpr int PL = D / 64;
+  const int lane = threadIdx.x & 63;
+  float M[G], Ls[G], o[G][PL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    M[g] = -INFINITY;
+    Ls[g] = 0.f;
+#pragma unroll
+    for (int k = 0; k < PL; ++k) o[g][k] = 0.f;
+  }
+  constexpr int NB = G <= 4 ? 4 : 2;                       // partials whose loads are in flight at once
+  for (int i0 = 0; i0 < n; i0 += NB) {
+    float m[NB][G], l[NB][G], x[NB][G][PL];
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+      const int i = min(i0 + r, n - 1);
+      const size_t base = (size_t(w0 + i) * 2 + ((i > 0 || w0_first) ? 0 : 1)) * G;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        m[r][g] = xload(a.part_ml + 2 * (base + g));
+        l[r][g] = xload(a.part_ml + 2 * (base + g) + 1);
+#pragma unroll
+        for (int k = 0; k < PL; ++k) x[r][g][k] = xload(a.part_acc + (base + g) * D + lane + 64 * k);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+      if (i0 + r >= n) break;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float mn = fmaxf(M[g], m[r][g]);
+        const float co = exp2f(M[g] - mn), cn = exp2f(m[r][g] - mn);
+        Ls[g] = fmaf(Ls[g], co, l[r][g] * cn);
+#pragma unroll
+        for (int k = 0; k < PL; ++k) o[g][k] = fmaf(o[g][k], co, x[r][g][k] * cn);
+        M[g] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float inv = 1.f / Ls[g];
+    const size_t ob = (size_t(seq) * a.num_q_heads + kvh * G + g) * D + lane;
+#pragma unroll
+    for (int k = 0; k < PL; ++k) {
+      const float r = o[g][k] * inv;
+      if constexpr (F32OUT) static_cast<float*>(a.out)[ob + 64 * k] = r;
+      else static_cast<uint16_t*>(a.out)[ob + 64 * k] = uint16_t(pack_bf16x2(r, 0.f) & 0xFFFFu);
+    }
+  }
+}
+
 // block_table and context_lens are separate restrict arguments so that the
 // compiler may read them through the scalar cache (s_load) even though the
 // kernel stores results: block ids then never wait behind in-flight tiles.
@@ -152,7 +248,9 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
   const int w = uniform(threadIdx.x >> 6);                // wave-uniform, so all range math stays scalar
   const int Hkv = a.num_kv_heads, Hq = a.num_q_heads;
   const int64_t U = int64_t(s_prefix[S]) * Hkv;
-  const int64_t W = min<int64_t>(a.total_waves, U);       // every range non-empty (see the reduce)
+  // at most U waves: every range is non-empty, so every wave from the first
+  // to the last of a split item holds a partial of it
+  const int64_t W = min<int64_t>(a.total_waves, U);
   const int wid = blockIdx.x * 4 + w;
   if (wid >= W) return;                                    // no work (no barrier follows)
   int64_t u = int64_t(wid) * U / W;
@@ -168,6 +266,95 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
   const uint32_t k_off = uint32_t((kr * D + kcol * C::EPL) * C::ES);
   const uint32_t v_off = uint32_t((vd * B + vs * C::TPL) * C::ES);
 
+  // Scalar cursor over the steps of this wave's range.  It runs ahead of the
+  // compute across (sequence, kv head) segments, so the first tiles of the
+  // next segment are in flight while the current one finishes; past the
+  // range it stays on the last step (a harmless re-read).
+  struct Cursor {
+    int64_t u;                  // first unit of the cursor's segment
+    int seq, kvh, part, p_end;  // segment: partitions [part, p_end) of (seq, kvh)
+    int blk, last_blk;          // first block of the step, last block of the segment
+    int st, nsteps;
+    bool live, any;             // any: some step of the range was ever found
+  };
+  auto seg_setup = [&](Cursor& c) {                          // derive the segment's steps
+    const int L = max(0, context_lens[c.seq]);
+    const int nu = units_of(L, PT);
+    c.p_end = int(min<int64_t>(nu, c.part + (u_end - c.u)));
+    const int t_begin = c.part * PT, t_end = min(L, c.p_end * PT);
+    c.nsteps = (max(t_end - t_begin, 0) + C::CH - 1) / C::CH;
+    c.blk = t_begin / B;
+    c.last_blk = max((t_end + B - 1) / B - 1, 0);
+    c.st = 0;
+  };
+  auto next_seg = [&](Cursor& c) -> bool {                   // false past the range
+    c.u += c.p_end - c.part;
+    if (c.u >= u_end) return false;
+    c.part = 0;
+    if (++c.kvh == Hkv) {
+      c.kvh = 0;
+      ++c.seq;
+    }
+    seg_setup(c);
+    return true;
+  };
+  auto skip_empty = [&](Cursor& c) {                         // first segment with a step, else dead
+    while (c.nsteps == 0) {
+      Cursor t = c;
+      if (!next_seg(t)) {
+        c.live = false;
+        return;
+      }
+      c = t;
+    }
+    c.any = true;
+  };
+  auto advance = [&](Cursor& c) {
+    if (!c.live) return;
+    if (c.st + 1 < c.nsteps) {
+      ++c.st;
+      c.blk += C::BPC;
+      return;
+    }
+    Cursor t = c;
+    if (!next_seg(t)) {
+      c.live = false;
+      return;
+    }
+    skip_empty(t);
+    if (t.live) c = t;
+    else c.live = false;
+  };
+  // block ids of the cursor's step (blocks past the segment re-read its last
+  // block, and everything past the segment's end is masked); a range with no
+  // token at all reads block 0, which always exists, and uses nothing of it
+  auto cursor_ids = [&](const Cursor& c, int (&ids)[C::BPC]) {
+    const int32_t* row = block_table + size_t(c.seq) * a.max_blocks_per_seq;
+#pragma unroll
+    for (int k = 0; k < C::BPC; ++k) ids[k] = c.any ? uniform(row[min(c.blk + k, c.last_blk)]) : 0;
+  };
+
+  LoadT kreg[C::BPC][C::KLB];
+  LoadT vreg[C::BPC][C::VLB];
+  auto load_k = [&](const int (&ids)[C::BPC], int kh) {
+#pragma unroll
+    for (int k = 0; k < C::BPC; ++k) {
+      const auto r = tile_rsrc(kpool + (uint64_t(uint32_t(ids[k])) * uint32_t(Hkv) + uint32_t(kh)) * kTile,
+                               uint32_t(kTile));
+#pragma unroll
+      for (int i = 0; i < C::KLB; ++i) buffer_load(r, k_off, uint32_t(i * C::RPL * D * C::ES), kreg[k][i]);
+    }
+  };
+  auto load_v = [&](const int (&ids)[C::BPC], int kh) {
+#pragma unroll
+    for (int k = 0; k < C::BPC; ++k) {
+      const auto r = tile_rsrc(vpool + (uint64_t(uint32_t(ids[k])) * uint32_t(Hkv) + uint32_t(kh)) * kTile,
+                               uint32_t(kTile));
+#pragma unroll
+      for (int j = 0; j < C::VLB; ++j) buffer_load(r, v_off, uint32_t(j * C::DPL * B * C::ES), vreg[k][j]);
+    }
+  };
+
   // first unit of the range -> (sequence, kv head, partition)
   int seq = find_seq(s_prefix, S, int(u / Hkv));
   int kvh, part;
@@ -177,37 +364,93 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
     kvh = uniform(r / nu);
     part = uniform(r - kvh * nu);
   }
-  bool first = true;
 
-  for (;;) {                                               // one (sequence, kv head) segment per pass
+  // query of the G heads of (sq, kh); register j holds head j ^ gray.  qf / qp
+  // serve the segment being computed, qfn / qpn receive the next segment's.
+  float qf[C::F32 ? G : 1][4], qfn[C::F32 ? G : 1][4];
+  uint32_t qp[C::F32 ? 1 : G][4], qpn[C::F32 ? 1 : G][4];
+  auto load_q = [&](auto& df, auto& dp, int sq, int kh) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int head = kh * G + (j ^ gray);
+      if constexpr (C::F32) {
+        const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) +
+                                                          (size_t(sq) * Hq + head) * D + kcol * 4);
+        df[j][0] = v.x; df[j][1] = v.y; df[j][2] = v.z; df[j][3] = v.w;
+      } else {
+        const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
+                                                        (size_t(sq) * Hq + head) * D + kcol * 8);
+        dp[j][0] = v.x; dp[j][1] = v.y; dp[j][2] = v.z; dp[j][3] = v.w;
+      }
+    }
+  };
+
+  // Pipeline: kreg / vreg hold the tiles of the step being computed; nx is
+  // the cursor of the step whose tiles are loaded next, its ids already in
+  // scalar registers.
+  Cursor nx{u, seq, kvh, part, 0, 0, 0, 0, 0, true, false};
+  seg_setup(nx);
+  skip_empty(nx);
+  int ids_nx[C::BPC];
+  cursor_ids(nx, ids_nx);
+  int kvh_nx = nx.kvh;
+  load_q(qf, qp, seq, kvh);
+  // The query and block ids must be in registers before the first tile is
+  // requested; an explicit wait here keeps the compiler from waiting on every
+  // in-flight tile (vmcnt(0)) at each step.
+  __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0) only
+  __builtin_amdgcn_sched_barrier(0);
+  load_k(ids_nx, kvh_nx);                                   // keys before values, as in the loop
+  __builtin_amdgcn_sched_barrier(0);
+  load_v(ids_nx, kvh_nx);
+  __builtin_amdgcn_sched_barrier(0);
+  advance(nx);
+  cursor_ids(nx, ids_nx);
+  kvh_nx = nx.kvh;
+
+  // Split items this wave holds a partial of (at most two: the first and the
+  // last of its range).  It counts itself in on them only once its whole range
+  // is done, so that no segment switch waits for stores or atomics.
+  struct Pending {
+    int seq, kvh, w0, n, w1;
+    bool w0_first;
+  };
+  Pending pend[2] = {{0, 0, 0, 1, 0, false}, {0, 0, 0, 1, 0, false}};
+  bool has_pend[2] = {false, false};
+
+  bool first = true;
+  bool q_ready = false;                                      // qfn / qpn hold this segment's query
+  for (;;) {                                                 // one (sequence, kv head) segment per pass
     const int L = max(0, context_lens[seq]);
     const int nu = units_of(L, PT);
     const int p_end = int(min<int64_t>(nu, part + (u_end - u)));
     const bool whole = part == 0 && p_end == nu;
     const int t_begin = part * PT;
     const int t_end = min(L, p_end * PT);
-    const int last_blk = max((t_end + B - 1) / B - 1, 0);  // absolute index of the segment's last block
-    const int blk0 = t_begin / B;
-    const int32_t* trow = block_table + size_t(seq) * a.max_blocks_per_seq;
-    const int nsteps = (t_end - t_begin + C::CH - 1) / C::CH;
+    const int nsteps = (max(t_end - t_begin, 0) + C::CH - 1) / C::CH;
+    // the next segment of the range (itself at the range's end): its query
+    // is fetched during this segment's last step
+    const bool has_next = u + (p_end - part) < u_end;
+    const int nq_kvh = has_next ? (kvh + 1 == Hkv ? 0 : kvh + 1) : kvh;
+    const int nq_seq = has_next && kvh + 1 == Hkv ? seq + 1 : seq;
 
     float sl = a.scale_log2;
     if constexpr (KV == KV_FP8) sl *= a.k_scale[kvh];
 
-    // query of the G heads; register j holds head j ^ gray
-    float qf[C::F32 ? G : 1][4];
-    uint32_t qp[C::F32 ? 1 : G][4];
+    if (!first) {
+      if (q_ready) {
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const int head = kvh * G + (j ^ gray);
-      if constexpr (C::F32) {
-        const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) +
-                                                          (size_t(seq) * Hq + head) * D + kcol * 4);
-        qf[j][0] = v.x; qf[j][1] = v.y; qf[j][2] = v.z; qf[j][3] = v.w;
-      } else {
-        const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
-                                                        (size_t(seq) * Hq + head) * D + kcol * 8);
-        qp[j][0] = v.x; qp[j][1] = v.y; qp[j][2] = v.z; qp[j][3] = v.w;
+        for (int j = 0; j < (C::F32 ? G : 1); ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) qf[j][e] = qfn[j][e];
+#pragma unroll
+        for (int j = 0; j < (C::F32 ? 1 : G); ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) qp[j][e] = qpn[j][e];
+      } else {                                               // after an empty segment
+        load_q(qf, qp, seq, kvh);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
@@ -220,190 +463,153 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
       for (int j = 0; j < C::VLB; ++j) acc[g][j] = 0.f;
     }
 
-    // block ids of a step (blocks past the segment re-read its last block;
-    // everything past t_end is masked)
-    auto step_ids = [&](int step, int (&ids)[C::BPC]) {
-#pragma unroll
-      for (int k = 0; k < C::BPC; ++k) ids[k] = uniform(trow[min(blk0 + step * C::BPC + k, last_blk)]);
-    };
-    LoadT kreg[C::BPC][C::KLB];
-    LoadT vreg[C::BPC][C::VLB];
-    auto load_k = [&](const int (&ids)[C::BPC]) {
-#pragma unroll
-      for (int k = 0; k < C::BPC; ++k) {
-        const auto r = tile_rsrc(kpool + (uint64_t(uint32_t(ids[k])) * uint32_t(Hkv) + uint32_t(kvh)) * kTile,
-                                 uint32_t(kTile));
-#pragma unroll
-        for (int i = 0; i < C::KLB; ++i) buffer_load(r, k_off, uint32_t(i * C::RPL * D * C::ES), kreg[k][i]);
-      }
-    };
-    auto load_v = [&](const int (&ids)[C::BPC]) {
-#pragma unroll
-      for (int k = 0; k < C::BPC; ++k) {
-        const auto r = tile_rsrc(vpool + (uint64_t(uint32_t(ids[k])) * uint32_t(Hkv) + uint32_t(kvh)) * kTile,
-                                 uint32_t(kTile));
-#pragma unroll
-        for (int j = 0; j < C::VLB; ++j) buffer_load(r, v_off, uint32_t(j * C::DPL * B * C::ES), vreg[k][j]);
-      }
-    };
-
-    int ids_cur[C::BPC], ids_nxt[C::BPC];
-    if (nsteps > 0) {                                        // an empty sequence reads nothing
-    step_ids(0, ids_cur);
-    step_ids(min(1, max(nsteps - 1, 0)), ids_nxt);
-    // The query and the first block ids must be in registers before the
-    // first tile is requested; an explicit wait here keeps the compiler
-    // from waiting on every in-flight tile (vmcnt(0)) at each step.
-    __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0) only
-    // Loads are unconditional so that the compiler counts them exactly
-    // (vmcnt(n) rather than vmcnt(0) at every use); a prefetch past the
-    // last step re-reads that step.
-    __builtin_amdgcn_sched_barrier(0);
-    load_k(ids_cur);                                          // keys before values, as in the loop
-    __builtin_amdgcn_sched_barrier(0);
-    load_v(ids_cur);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int st = 0; st < nsteps; ++st) {
+    // One 64-token step.  The last step of a segment also fetches the next
+    // segment's query, ahead of the next tiles, so that the wait for those
+    // tiles covers it.
+    auto do_step = [&](int st, auto last_step) {
       const int cs = t_begin + st * C::CH;
 
-      // ---- scores (tokens past t_end are masked in the softmax)
-#pragma unroll
-      for (int k = 0; k < C::BPC; ++k) {
-#pragma unroll
-        for (int i = 0; i < C::KLB; ++i) {
-          float pt[G];
-          if constexpr (C::F32) {
-            const uint4 x = kreg[k][i];
-            const float kf[4] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
-                                 __uint_as_float(x.w)};
-#pragma unroll
-            for (int j = 0; j < G; ++j)
-              pt[j] = fmaf(kf[3], qf[j][3], fmaf(kf[2], qf[j][2], fmaf(kf[1], qf[j][1], kf[0] * qf[j][0])));
-          } else {
-            uint32_t kp[4];
-            load_pairs<KV>(kreg[k][i], kp);
-#pragma unroll
-            for (int j = 0; j < G; ++j)
-              pt[j] = dot2_bf16(kp[3], qp[j][3],
-                                dot2_bf16(kp[2], qp[j][2], dot2_bf16(kp[1], qp[j][1], dot2_bf16(kp[0], qp[j][0], 0.f))));
-          }
-          if constexpr (G >= 8) {
-#pragma unroll
-            for (int x = 0; x < 4; ++x) pt[x] += dpp<DPP_HALF_MIRROR>(pt[x + 4]);
-          }
-          if constexpr (G >= 4) {
-#pragma unroll
-            for (int x = 0; x < 2; ++x) pt[x] += dpp<DPP_QP_XOR3>(pt[x + 2]);
-          }
-          if constexpr (G >= 2) pt[0] += dpp<DPP_QP_XOR1>(pt[1]);
-          float sc = pt[0];
-#pragma unroll
-          for (int sp = G; sp < C::LPR; sp *= 2) {
-            if constexpr (C::LPR == 16) {
-              if (sp == 1) sc += dpp<DPP_ROW_ROR(1)>(sc);
-              else if (sp == 2) sc += dpp<DPP_ROW_ROR(2)>(sc);
-              else if (sp == 4) sc += dpp<DPP_ROW_ROR(4)>(sc);
-              else sc += dpp<DPP_ROW_ROR(8)>(sc);
+        // ---- scores (tokens past t_end are masked in the softmax)
+  #pragma unroll
+        for (int k = 0; k < C::BPC; ++k) {
+  #pragma unroll
+          for (int i = 0; i < C::KLB; ++i) {
+            float pt[G];
+            if constexpr (C::F32) {
+              const uint4 x = kreg[k][i];
+              const float kf[4] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
+                                   __uint_as_float(x.w)};
+  #pragma unroll
+              for (int j = 0; j < G; ++j)
+                pt[j] = fmaf(kf[3], qf[j][3], fmaf(kf[2], qf[j][2], fmaf(kf[1], qf[j][1], kf[0] * qf[j][0])));
             } else {
-              sc += __shfl_xor(sc, sp);
+              uint32_t kp[4];
+              load_pairs<KV>(kreg[k][i], kp);
+  #pragma unroll
+              for (int j = 0; j < G; ++j)
+                pt[j] = dot2_bf16(kp[3], qp[j][3],
+                                  dot2_bf16(kp[2], qp[j][2], dot2_bf16(kp[1], qp[j][1], dot2_bf16(kp[0], qp[j][0], 0.f))));
             }
-          }
-          // every lane writes; the lanes of one (token, head) hold the same sum
-          s_score[w][(k * B + i * C::RPL + kr) * G + gray] = sc;
-        }
-      }
-      // The scheduler must not move loads across these phase boundaries: the
-      // next step's K tile goes out after the scores and its V tile after
-      // the PV, which is what lets each use wait for half the loads in flight.
-      __builtin_amdgcn_sched_barrier(0);
-      load_k(ids_nxt);                                        // next step's keys fly during softmax + PV
-      __builtin_amdgcn_sched_barrier(0);
-      wave_lds_sync();
-
-      // ---- online softmax over this step, one token per lane
-      const bool valid = lane < C::CH && cs + lane < t_end;
-      float pv[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        // raw scores; the positive scale sl (log2 units) is applied inside exp2
-        const float sv = valid ? s_score[w][min(lane, C::CH - 1) * G + g] : -INFINITY;
-        const float mn = fmaxf(m_run[g], wave_max(sv));
-        const float al = exp2f((m_run[g] - mn) * sl);
-        pv[g] = exp2f(fmaf(sv, sl, -mn * sl));
-        l_lane[g] = fmaf(l_lane[g], al, pv[g]);
-#pragma unroll
-        for (int j = 0; j < C::VLB; ++j) acc[g][j] *= al;
-        m_run[g] = mn;
-      }
-      if (lane < C::CH) {
-        if constexpr (C::F32) {
-#pragma unroll
-          for (int g = 0; g < G; ++g) reinterpret_cast<float*>(s_p[w])[g * C::CH + lane] = pv[g];
-        } else {
-#pragma unroll
-          for (int g = 0; g < G; ++g)
-            reinterpret_cast<uint16_t*>(s_p[w])[g * C::CH + lane] = uint16_t(pack_bf16x2(pv[g], 0.f) & 0xFFFFu);
-        }
-      }
-      wave_lds_sync();
-
-      // ---- PV (values of tokens past t_end may be NaN poison: zeroed by select)
-#pragma unroll
-      for (int k = 0; k < C::BPC; ++k) {
-        const int tok0 = k * B + vs * C::TPL;                // step-relative first token of this lane's segment
-        const bool tail = cs + k * B + B > t_end;           // block holds tokens past the end
-        if constexpr (C::F32) {
-          float pf[G][4];
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const float4 t = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(s_p[w]) + g * C::CH + tok0);
-            pf[g][0] = t.x; pf[g][1] = t.y; pf[g][2] = t.z; pf[g][3] = t.w;
-          }
-#pragma unroll
-          for (int j = 0; j < C::VLB; ++j) {
-            const uint4 x = vreg[k][j];
-            float v[4] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w)};
-            if (tail) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = (cs + tok0 + e < t_end) ? v[e] : 0.f;
+            if constexpr (G >= 8) {
+  #pragma unroll
+              for (int x = 0; x < 4; ++x) pt[x] += dpp<DPP_HALF_MIRROR>(pt[x + 4]);
             }
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-              acc[g][j] = fmaf(v[3], pf[g][3], fmaf(v[2], pf[g][2], fmaf(v[1], pf[g][1], fmaf(v[0], pf[g][0], acc[g][j]))));
-          }
-        } else {
-          uint32_t pp[G][4];
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const uint4 t = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(s_p[w]) + g * C::CH + tok0);
-            pp[g][0] = t.x; pp[g][1] = t.y; pp[g][2] = t.z; pp[g][3] = t.w;
-          }
-#pragma unroll
-          for (int j = 0; j < C::VLB; ++j) {
-            uint32_t vp[4];
-            load_pairs<KV>(vreg[k][j], vp);
-            if (tail) {
-#pragma unroll
-              for (int m = 0; m < 4; ++m) {
-                const int t = cs + tok0 + 2 * m;
-                vp[m] &= (t < t_end ? 0x0000FFFFu : 0u) | (t + 1 < t_end ? 0xFFFF0000u : 0u);
+            if constexpr (G >= 4) {
+  #pragma unroll
+              for (int x = 0; x < 2; ++x) pt[x] += dpp<DPP_QP_XOR3>(pt[x + 2]);
+            }
+            if constexpr (G >= 2) pt[0] += dpp<DPP_QP_XOR1>(pt[1]);
+            float sc = pt[0];
+  #pragma unroll
+            for (int sp = G; sp < C::LPR; sp *= 2) {
+              if constexpr (C::LPR == 16) {
+                if (sp == 1) sc += dpp<DPP_ROW_ROR(1)>(sc);
+                else if (sp == 2) sc += dpp<DPP_ROW_ROR(2)>(sc);
+                else if (sp == 4) sc += dpp<DPP_ROW_ROR(4)>(sc);
+                else sc += dpp<DPP_ROW_ROR(8)>(sc);
+              } else {
+                sc += __shfl_xor(sc, sp);
               }
             }
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-              acc[g][j] = dot2_bf16(vp[3], pp[g][3], dot2_bf16(vp[2], pp[g][2],
-                          dot2_bf16(vp[1], pp[g][1], dot2_bf16(vp[0], pp[g][0], acc[g][j]))));
+            // every lane writes; the lanes of one (token, head) hold the same sum
+            s_score[w][(k * B + i * C::RPL + kr) * G + gray] = sc;
           }
         }
-      }
+        // The scheduler must not move loads across these phase boundaries: the
+        // next step's K tile goes out after the scores and its V tile after
+        // the PV, which is what lets each use wait for half the loads in flight.
+        __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(last_step)::value) load_q(qfn, qpn, nq_seq, nq_kvh);
+      load_k(ids_nx, kvh_nx);                                 // the next step's keys fly during softmax + PV
       __builtin_amdgcn_sched_barrier(0);
-      load_v(ids_nxt);                                        // next step's values fly during its scores
+        wave_lds_sync();
+
+        // ---- online softmax over this step, one token per lane
+        const bool valid = lane < C::CH && cs + lane < t_end;
+        float pv[G];
+  #pragma unroll
+        for (int g = 0; g < G; ++g) {
+          // raw scores; the positive scale sl (log2 units) is applied inside exp2
+          const float sv = valid ? s_score[w][min(lane, C::CH - 1) * G + g] : -INFINITY;
+          const float mn = fmaxf(m_run[g], wave_max(sv));
+          const float al = exp2f((m_run[g] - mn) * sl);
+          pv[g] = exp2f(fmaf(sv, sl, -mn * sl));
+          l_lane[g] = fmaf(l_lane[g], al, pv[g]);
+  #pragma unroll
+          for (int j = 0; j < C::VLB; ++j) acc[g][j] *= al;
+          m_run[g] = mn;
+        }
+        if (lane < C::CH) {
+          if constexpr (C::F32) {
+  #pragma unroll
+            for (int g = 0; g < G; ++g) reinterpret_cast<float*>(s_p[w])[g * C::CH + lane] = pv[g];
+          } else {
+  #pragma unroll
+            for (int g = 0; g < G; ++g)
+              reinterpret_cast<uint16_t*>(s_p[w])[g * C::CH + lane] = uint16_t(pack_bf16x2(pv[g], 0.f) & 0xFFFFu);
+          }
+        }
+        wave_lds_sync();
+
+        // ---- PV (values of tokens past t_end may be NaN poison: zeroed by select)
+  #pragma unroll
+        for (int k = 0; k < C::BPC; ++k) {
+          const int tok0 = k * B + vs * C::TPL;                // step-relative first token of this lane's segment
+          const bool tail = cs + k * B + B > t_end;           // block holds tokens past the end
+          if constexpr (C::F32) {
+            float pf[G][4];
+  #pragma unroll
+            for (int g = 0; g < G; ++g) {
+              const float4 t = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(s_p[w]) + g * C::CH + tok0);
+              pf[g][0] = t.x; pf[g][1] = t.y; pf[g][2] = t.z; pf[g][3] = t.w;
+            }
+  #pragma unroll
+            for (int j = 0; j < C::VLB; ++j) {
+              const uint4 x = vreg[k][j];
+              float v[4] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w)};
+              if (tail) {
+  #pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (cs + tok0 + e < t_end) ? v[e] : 0.f;
+              }
+  #pragma unroll
+              for (int g = 0; g < G; ++g)
+                acc[g][j] = fmaf(v[3], pf[g][3], fmaf(v[2], pf[g][2], fmaf(v[1], pf[g][1], fmaf(v[0], pf[g][0], acc[g][j]))));
+            }
+          } else {
+            uint32_t pp[G][4];
+  #pragma unroll
+            for (int g = 0; g < G; ++g) {
+              const uint4 t = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(s_p[w]) + g * C::CH + tok0);
+              pp[g][0] = t.x; pp[g][1] = t.y; pp[g][2] = t.z; pp[g][3] = t.w;
+            }
+  #pragma unroll
+            for (int j = 0; j < C::VLB; ++j) {
+              uint32_t vp[4];
+              load_pairs<KV>(vreg[k][j], vp);
+              if (tail) {
+  #pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                  const int t = cs + tok0 + 2 * m;
+                  vp[m] &= (t < t_end ? 0x0000FFFFu : 0u) | (t + 1 < t_end ? 0xFFFF0000u : 0u);
+                }
+              }
+  #pragma unroll
+              for (int g = 0; g < G; ++g)
+                acc[g][j] = dot2_bf16(vp[3], pp[g][3], dot2_bf16(vp[2], pp[g][2],
+                            dot2_bf16(vp[1], pp[g][1], dot2_bf16(vp[0], pp[g][0], acc[g][j]))));
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      load_v(ids_nx, kvh_nx);                                 // its values fly during its scores
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int k = 0; k < C::BPC; ++k) ids_cur[k] = ids_nxt[k];
-      step_ids(min(st + 2, max(nsteps - 1, 0)), ids_nxt);     // ids one step ahead of their loads
-    }
-    }
+      advance(nx);                                            // ids one step ahead of their loads
+      cursor_ids(nx, ids_nx);
+      kvh_nx = nx.kvh;
+    };
+    for (int st = 0; st + 1 < nsteps; ++st) do_step(st, std::false_type{});
+    q_ready = nsteps > 0;
+    if (nsteps > 0) do_step(nsteps - 1, std::true_type{});
 
     // ---- finish the segment
     float l[G];
@@ -437,18 +643,24 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
       }
     } else {
       // split (sequence, kv head): slot 0 holds the range's first item, slot 1 its last
-      const size_t base = (size_t(wid) * 2 + (first ? 0 : 1)) * G;
+      const int slot = first ? 0 : 1;
+      const size_t base = (size_t(wid) * 2 + slot) * G;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         if (lane == 0) {
-          a.part_ml[2 * (base + g)] = m_run[g] * sl;        // log2 units
-          a.part_ml[2 * (base + g) + 1] = l[g];
+          xstore(a.part_ml + 2 * (base + g), m_run[g] * sl);  // log2 units
+          xstore(a.part_ml + 2 * (base + g) + 1, l[g]);
         }
         if (vs == 0) {
 #pragma unroll
-          for (int j = 0; j < C::VLB; ++j) a.part_acc[(base + g) * D + j * C::DPL + vd] = acc[g][j];
+          for (int j = 0; j < C::VLB; ++j) xstore(a.part_acc + (base + g) * D + j * C::DPL + vd, acc[g][j]);
         }
       }
+      const int64_t u0 = int64_t(s_prefix[seq]) * Hkv + int64_t(kvh) * nu;
+      const int w0 = owner_wave(u0, U, W);
+      const int w1 = owner_wave(u0 + nu - 1, U, W);
+      pend[slot] = Pending{seq, kvh, w0, w1 - w0 + 1, w1, int64_t(w0) * U / W == u0};
+      has_pend[slot] = true;
     }
 
     u += p_end - part;
@@ -460,69 +672,14 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
       ++seq;
     }
   }
-}
 
-// Merge of split (sequence, kv head) items: one wave per (sequence, query
-// head) finds the waves whose ranges cut through its item and combines their
-// partials, out = sum_w e^(m_w - M) acc_w / sum_w e^(m_w - M) l_w.
-template <int D, int G, bool F32OUT>
-__global__ void __launch_bounds__(256) decode_reduce_kernel(DecodeArgs a) {
-  extern __shared__ int s_prefix[];
-  __shared__ int s_tmp[256];
-  const int S = a.num_seqs, PT = a.part_tokens;
-  build_prefix(a.context_lens, S, PT, s_prefix, s_tmp);
-  const int lane = threadIdx.x & 63;
-  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
-  if (pair >= S * Hq) return;
-  const int seq = pair / Hq, head = pair - seq * Hq;
-  const int kvh = head / G, g = head - kvh * G;
-  const int64_t U = int64_t(s_prefix[S]) * Hkv;
-  // As in the partition kernel: with at most U waves no range is empty, so
-  // every wave from w0 to w1 holds a partial of this item.
-  const int64_t W = min<int64_t>(a.total_waves, U);
-  const int nu = units_of(a.context_lens[seq], PT);
-  const int64_t u0 = int64_t(s_prefix[seq]) * Hkv + int64_t(kvh) * nu;
-  const int w0 = owner_wave(u0, U, W);
-  const int w1 = owner_wave(u0 + nu - 1, U, W);
-  if (w0 == w1) return;                                    // written by the partition kernel
-  const bool w0_starts_here = int64_t(w0) * U / W == u0;   // then the item is w0's first
-  const int n = w1 - w0 + 1;
-  auto slot_base = [&](int i) -> size_t {                  // partial of the i-th wave over the item
-    const int wv = w0 + i;
-    const int slot = (i > 0 || w0_starts_here) ? 0 : 1;
-    return (size_t(wv) * 2 + slot) * G + g;
-  };
-  float M = -INFINITY;
-  for (int p0 = 0; p0 < n; p0 += 64) {
-    const int p = p0 + lane;
-    const float mp = p < n ? a.part_ml[2 * slot_base(p)] : -INFINITY;
-    M = fmaxf(M, wave_max(mp));
-  }
-  float Ls = 0.f;
-  float o[D / 64];
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) o[i] = 0.f;
-  for (int p0 = 0; p0 < n; p0 += 64) {
-    const int p = p0 + lane;
-    const float wp = p < n ? exp2f(a.part_ml[2 * slot_base(p)] - M) : 0.f;
-    const float lp = p < n ? a.part_ml[2 * slot_base(p) + 1] : 0.f;
-    Ls += wave_sum(wp * lp);
-    const int cnt = min(64, n - p0);
-    for (int q = 0; q < cnt; ++q) {
-      const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wp), q));
-      const float* src = a.part_acc + slot_base(p0 + q) * D;
-#pragma unroll
-      for (int i = 0; i < D / 64; ++i) o[i] = fmaf(wq, src[lane + 64 * i], o[i]);
-    }
-  }
-  const float inv = 1.f / Ls;
-  const size_t ob = size_t(pair) * D;
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) {
-    const float r = o[i] * inv;
-    if constexpr (F32OUT) static_cast<float*>(a.out)[ob + lane + 64 * i] = r;
-    else static_cast<uint16_t*>(a.out)[ob + lane + 64 * i] = uint16_t(pack_bf16x2(r, 0.f) & 0xFFFFu);
+  // Count in on the split items; the last wave to arrive at one merges it.
+  if (has_pend[0] || has_pend[1]) {
+    bool last0, last1;
+    arrive_last2(a.arrivals + pend[0].w1, pend[0].n, has_pend[0], a.arrivals + pend[1].w1, pend[1].n, has_pend[1],
+                 last0, last1);
+    if (last0) merge_split<D, G, C::F32>(a, pend[0].seq, pend[0].kvh, pend[0].w0, pend[0].n, pend[0].w0_first);
+    if (last1) merge_split<D, G, C::F32>(a, pend[1].seq, pend[1].kvh, pend[1].w0, pend[1].n, pend[1].w0_first);
   }
 }
 
@@ -552,11 +709,6 @@ hipError_t launch_decode_t(const DecodeArgs& a0, int64_t upper_units, hipStream_
   DecodeArgs a = a0;
   a.total_waves = int32_t(wgs * 4);
   hipLaunchKernelGGL(kern, dim3(uint32_t(wgs)), dim3(256), lds, s, a, a.block_table, a.context_lens);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t pairs = int64_t(a.num_seqs) * a.num_q_heads;
-  hipLaunchKernelGGL((decode_reduce_kernel<D, G, KV == KV_F32>), dim3(uint32_t((pairs + 3) / 4)), dim3(256), lds, s,
-                     a);
   return hipGetLastError();
 }
 

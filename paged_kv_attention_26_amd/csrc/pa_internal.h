@@ -40,6 +40,7 @@ struct DecodeArgs {
   const int32_t* context_lens;
   float* part_ml;     // [total_waves][2][G][2]  (running max in log2 units, sum) of split items
   float* part_acc;    // [total_waves][2][G][head_dim]
+  int32_t* arrivals;  // [kDecodeMaxWaves] per split item (keyed by its last wave); zero between calls
   float scale_log2;   // softmax scale * log2(e)
   int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq;
   int32_t part_tokens, total_waves;  // total_waves is set by the launcher
@@ -63,7 +64,7 @@ struct PrefillArgs {
 };
 
 struct DecodeWorkspace {
-  size_t ml_off, acc_off, total;
+  size_t arrivals_off, ml_off, acc_off, total;
 };
 
 // Record the message of a failed call for pa_last_error(); returns code.

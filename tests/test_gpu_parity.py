@@ -117,17 +117,28 @@ def test_decode_matches_oracle(name, part):
 
 
 def test_decode_repeated_calls_reuse_the_workspace():
-    """Back-to-back calls on one workspace give bit-identical results."""
+    """Calls of different shapes and partition sizes, interleaved on one
+    workspace, repeat bit-identically, and every call leaves the per-item
+    arrival counters (the workspace's first 4096 int32) at zero."""
     from paged_kv_attention_26_amd import binding as pa, runner
-    batch = W.config3(16, small=True)
-    g = runner.prepare(batch)
-    runner.store_step(g)
-    d = g.dec
-    ws = pa.decode_workspace(len(d["idx"]), batch.num_q_heads, batch.head_dim, d["max_len"], 64)
-    outs = [runner.decode_step(g, partition_tokens=64, workspace=ws).clone() for _ in range(5)]
-    torch.cuda.synchronize()
-    for o in outs[1:]:
-        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    batches = [W.config3(16, small=True), W.config2(small=True), skew_batch()]
+    gs = []
+    for b in batches:
+        g = runner.prepare(b)
+        runner.store_step(g)
+        gs.append(g)
+    ws = pa.decode_workspace(1, 1, 128, 1, 0)
+    first = {}
+    for rep in range(3):
+        for i, g in enumerate(gs):
+            for part in (0, 128):
+                o = runner.decode_step(g, partition_tokens=part, workspace=ws).clone()
+                torch.cuda.synchronize()
+                assert int(torch.count_nonzero(ws[:4096 * 4])) == 0, (i, part, rep)
+                if (i, part) in first:
+                    assert torch.equal(o.view(torch.int16), first[(i, part)].view(torch.int16)), (i, part, rep)
+                else:
+                    first[(i, part)] = o
 
 
 def test_block_permutation_leaves_output_bit_identical():
