@@ -9,9 +9,13 @@
 //
 // How (QK^T and PV are dense contractions, so they run on MFMA; bf16 in,
 // fp32 accumulate):
-//  * A wave owns 32 query rows of one query head; the waves of a workgroup
-//    share a kv head (the G heads of a group, or neighbouring query tiles),
-//    so the K/V tiles they read are shared through the CU's L1.
+//  * A wave owns 32 query rows of one query head; the four waves of a
+//    workgroup share a kv head (the G heads of a group, or neighbouring query
+//    tiles).  The workgroup stages each 32-key K / V^T tile once into LDS
+//    (rows padded so that the MFMA operand reads are free of bank conflicts),
+//    double-buffered: the next tile's global loads fly while the current
+//    tile's MFMAs run, one barrier per tile.  Block ids come through the
+//    scalar cache.  Two workgroups fit on a CU.
 //  * Scores are formed transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 //    (keys are MFMA rows, queries columns): every lane then owns one query
 //    column, and the softmax statistics and the rescaling of O^T stay in the
@@ -47,12 +51,21 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const
 __device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
 template <int B, int G>
-__global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a, const int32_t* __restrict__ block_table,
+                                                        const int32_t* __restrict__ cu_q_lens,
+                                                        const int32_t* __restrict__ seq_lens) {
   constexpr int D = 128;
   constexpr int QT = 32;                 // query rows per wave
   constexpr int KT = 32;                 // keys per tile
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  constexpr int KROW = D * 2 + 16;       // LDS bytes per key row (16 bytes of padding: conflict-free operand reads)
+  constexpr int VROW = KT * 2 + 16;      // LDS bytes per head-dim row of the transposed value tile
+  constexpr int KBUF = KT * KROW;
+  constexpr int BUF = KBUF + D * VROW;
+  __shared__ __attribute__((aligned(16))) char smem[2][BUF];   // double-buffered K / V^T tile
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
   const int hh = lane >> 5;              // lane half: k-slice of operands, row group of accumulators
   const int n = lane & 31;               // query column / operand row
   const int Hkv = a.num_kv_heads, Hq = a.num_q_heads;
@@ -62,33 +75,76 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
   const int xcd = id & 7;
   const int k8 = id >> 3;
   const int pair = (k8 / a.wg_per_pair) * 8 + xcd;
-  if (pair >= a.num_seqs * Hkv) return;
+  if (pair >= a.num_seqs * Hkv) return;                  // whole workgroup
   const int grp = k8 % a.wg_per_pair;
   const int seq = pair / Hkv, kvh = pair - seq * Hkv;
+  const int q0 = cu_q_lens[seq];
+  const int q_len = cu_q_lens[seq + 1] - q0;
+  const int total = seq_lens[seq];
+  const int P = total - q_len;
+  // wave w serves query head kvh * G + (col % G) on query tile qt (heavy, late tiles first)
+  auto tile_of = [&](int wv) { return a.num_qtiles - 1 - (grp * 4 + wv) / G; };
+  auto key_end_of = [&](int wv) {                        // keys the wave's last row needs; 0 if idle
+    const int t = tile_of(wv);
+    return (t >= 0 && t * QT < q_len) ? P + min(q_len, (t + 1) * QT) : 0;
+  };
+  // the workgroup streams the keys any of its waves needs
+  const int key_end_wg = max(max(key_end_of(0), key_end_of(1)), max(key_end_of(2), key_end_of(3)));
+  if (key_end_wg <= 0) return;                           // whole workgroup
+  const int n_tiles_wg = (key_end_wg + KT - 1) / KT;
+  const int kmax = key_end_wg - 1;
   const int col = grp * 4 + w;
   const int h_local = col % G;
-  const int qt = a.num_qtiles - 1 - col / G;            // heavy (late) query tiles first
-  if (qt < 0) return;
-  const int q0 = a.cu_q_lens[seq];
-  const int q_len = a.cu_q_lens[seq + 1] - q0;
-  if (qt * QT >= q_len) return;
-  const int total = a.seq_lens[seq];
-  const int P = total - q_len;
+  const int qt = tile_of(w);
+  const int key_end = key_end_of(w);
+  const int n_tiles = (key_end + KT - 1) / KT;          // 0 for an idle wave
   const int head = kvh * G + h_local;
   const int t = qt * QT + n;                            // this lane's chunk row
-  const bool valid_q = t < q_len;
+  const bool valid_q = key_end > 0 && t < q_len;
   const int pos = P + t;                                 // absolute position of the query
-  const int key_end = P + min(q_len, (qt + 1) * QT);     // keys the tile's last row needs
-  const int n_tiles = (key_end + KT - 1) / KT;
-  const int* table = a.block_table + size_t(seq) * a.max_blocks_per_seq;
+  const int32_t* table = block_table + size_t(seq) * a.max_blocks_per_seq;
   const char* kpool = static_cast<const char*>(a.k_cache);
   const char* vpool = static_cast<const char*>(a.v_cache);
   const float c = a.scale_log2;
 
+  // ---- staging of one tile by the whole workgroup: each thread moves two
+  // 16-byte chunks of K (rows kr0, kr0 + 16; column chunk kcc) and two of V^T
+  // (head dims vd0, vd0 + 64; 8-key group vkc).  Keys past the workgroup's
+  // range re-read its last key (their scores are masked, their V zeroed).
+  const int kr0 = tid >> 4, kcc = tid & 15;
+  const int vd0 = tid >> 2, vkc = tid & 3;
+  uint4 kst0, kst1, vst0, vst1;
+  auto stage_load = [&](int kt, int id0, int id1) __attribute__((always_inline)) {
+    const int k0 = kt * KT;
+    const int b0 = k0 / B;
+    const int key0 = min(k0 + kr0, kmax), key1 = min(k0 + kr0 + 16, kmax);
+    const int bk0 = key0 / B == b0 ? id0 : id1, bk1 = key1 / B == b0 ? id0 : id1;
+    kst0 = *reinterpret_cast<const uint4*>(kpool + ((size_t(bk0) * Hkv + kvh) * B + key0 % B) * (D * 2) + kcc * 16);
+    kst1 = *reinterpret_cast<const uint4*>(kpool + ((size_t(bk1) * Hkv + kvh) * B + key1 % B) * (D * 2) + kcc * 16);
+    const int kb = min(k0 + 8 * vkc, kmax & ~7);
+    const int bv = kb / B == b0 ? id0 : id1;
+    const char* vsrc = vpool + ((size_t(bv) * Hkv + kvh) * D + vd0) * (B * 2) + (kb % B) * 2;
+    vst0 = *reinterpret_cast<const uint4*>(vsrc);
+    vst1 = *reinterpret_cast<const uint4*>(vsrc + 64 * (B * 2));
+  };
+  auto stage_store = [&](int buf) __attribute__((always_inline)) {
+    char* sb = smem[buf];
+    *reinterpret_cast<uint4*>(sb + kr0 * KROW + kcc * 16) = kst0;
+    *reinterpret_cast<uint4*>(sb + (kr0 + 16) * KROW + kcc * 16) = kst1;
+    *reinterpret_cast<uint4*>(sb + KBUF + vd0 * VROW + vkc * 16) = vst0;
+    *reinterpret_cast<uint4*>(sb + KBUF + (vd0 + 64) * VROW + vkc * 16) = vst1;
+  };
+  // block ids of a tile's (at most two) blocks, read through the scalar cache
+  auto tile_ids = [&](int kt, int& id0, int& id1) __attribute__((always_inline)) {
+    const int b0 = kt * KT / B;
+    id0 = table[min(b0, kmax / B)];
+    id1 = table[min(b0 + 1, kmax / B)];
+  };
+
   // ---- Q^T as 8 B operands (k = 16 head dims each): row q0 + t, dims 16s + 8hh .. + 7
   uint4 qb[8];
   {
-    const int row = q0 + min(t, q_len - 1);
+    const int row = q0 + max(0, min(t, q_len - 1));
     const uint16_t* qr = static_cast<const uint16_t*>(a.q) + (size_t(row) * Hq + head) * D + 8 * hh;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qb[s] = *reinterpret_cast<const uint4*>(qr + 16 * s);
@@ -101,87 +157,95 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
   const int my_key = swap23(n);                          // key of MFMA row n within a tile
   const int first_row_pos = P + qt * QT;                 // smallest query position of the tile
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int k0 = kt * KT;
-    // ---- S^T = K Q^T  (A: lane row n = key k0 + my_key, dims 16s + 8hh)
-    uint4 ka[8];
-    {
-      const int key = min(k0 + my_key, key_end - 1);
-      const int blk = table[key / B];
-      const char* kr = kpool + ((size_t(blk) * Hkv + kvh) * B + key % B) * (D * 2) + 16 * hh;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) ka[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
-    }
-    // V^T operands: d-tile dt (dims 32dt + n), key slice ks (keys k0 + 16ks + 8hh .. + 7)
-    uint4 va[4][2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int kb = min(k0 + 16 * ks, key_end - 1);
-      const int blk = table[kb / B];
-      const int off = (B == 16 ? 0 : (k0 + 16 * ks) % B) + 8 * hh;
-      const char* vb = vpool + (size_t(blk) * Hkv + kvh) * size_t(D * B * 2) + off * 2;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        va[dt][ks] = *reinterpret_cast<const uint4*>(vb + size_t(32 * dt + n) * (B * 2));
-    }
-    f32x16_t s = f32x16_t{};
-#pragma unroll
-    for (int st = 0; st < 8; ++st) s = mfma32(ka[st], qb[st], s);
+  int id0, id1, nid0, nid1;
+  tile_ids(0, id0, id1);
+  stage_load(0, id0, id1);
+  tile_ids(min(1, n_tiles_wg - 1), nid0, nid1);
+  stage_store(0);
+  __syncthreads();
 
-    // accumulator r = 4i + j holds MFMA row 8i + 4hh + j, i.e. key k0 + swap23(8i + 4hh + j)
-    if (k0 + KT - 1 > first_row_pos) {                   // tile reaches the diagonal or the end
+  for (int kt = 0; kt < n_tiles_wg; ++kt) {
+    // next tile's global loads fly during this tile's MFMAs (the last tile re-reads itself)
+    stage_load(min(kt + 1, n_tiles_wg - 1), nid0, nid1);
+    tile_ids(min(kt + 2, n_tiles_wg - 1), nid0, nid1);
+    const char* sb = smem[kt & 1];
+
+    if (kt < n_tiles) {
+      const int k0 = kt * KT;
+      // ---- S^T = K Q^T  (A: lane row n = key k0 + my_key, dims 16s + 8hh)
+      uint4 ka[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + swap23(8 * (r >> 2) + 4 * hh + (r & 3));
-        s[r] = (key <= pos && key < key_end) ? s[r] : -INFINITY;
-      }
-    }
-    float mt = s[0];
+      for (int s = 0; s < 8; ++s) ka[s] = *reinterpret_cast<const uint4*>(sb + my_key * KROW + (16 * s + 8 * hh) * 2);
+      f32x16_t sc = f32x16_t{};
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    if (__any(m_new > m_run)) {
-      const float al = exp2f((m_run - m_new) * c);
-      l_run *= al;
+      for (int st = 0; st < 8; ++st) sc = mfma32(ka[st], qb[st], sc);
+
+      // accumulator r = 4i + j holds MFMA row 8i + 4hh + j, i.e. key k0 + swap23(8i + 4hh + j)
+      if (k0 + KT - 1 > first_row_pos) {                 // tile reaches the diagonal or the end
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= al;
-      m_run = m_new;
-    }
-    const float mc = m_run * c;
-    float p[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[r] = exp2f(fmaf(s[r], c, -mc));
-      l_run += p[r];
-    }
-    // P^T operands: key slice ks takes accumulators 8ks .. 8ks + 7 (keys k0 + 16ks + 8hh + 0..7)
-    uint4 pb[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      pb[ks] = make_uint4(pack_bf16x2(p[8 * ks + 0], p[8 * ks + 1]), pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]),
-                          pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]), pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7]));
-    if (k0 + KT > key_end) {                              // zero V rows of keys past the end (NaN poison)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int kb = k0 + 16 * ks + 8 * hh;
-        uint32_t msk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          msk[e] = (kb + 2 * e < key_end ? 0x0000FFFFu : 0u) | (kb + 2 * e + 1 < key_end ? 0xFFFF0000u : 0u);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          va[dt][ks].x &= msk[0]; va[dt][ks].y &= msk[1]; va[dt][ks].z &= msk[2]; va[dt][ks].w &= msk[3];
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + swap23(8 * (r >> 2) + 4 * hh + (r & 3));
+          sc[r] = (key <= pos && key < key_end) ? sc[r] : -INFINITY;
         }
       }
-    }
+      float mt = sc[0];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      o[dt] = mfma32(va[dt][0], pb[0], o[dt]);
-      o[dt] = mfma32(va[dt][1], pb[1], o[dt]);
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float m_new = fmaxf(m_run, mt);
+      if (__any(m_new > m_run)) {
+        const float al = exp2f((m_run - m_new) * c);
+        l_run *= al;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= al;
+        m_run = m_new;
+      }
+      const float mc = m_run * c;
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = exp2f(fmaf(sc[r], c, -mc));
+        l_run += p[r];
+      }
+      // P^T operands: key slice ks takes accumulators 8ks .. 8ks + 7 (keys k0 + 16ks + 8hh + 0..7)
+      uint4 pb[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        pb[ks] = make_uint4(pack_bf16x2(p[8 * ks + 0], p[8 * ks + 1]), pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]),
+                            pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]), pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7]));
+      // V^T operands: d-tile dt (dims 32dt + n), key slice ks (keys k0 + 16ks + 8hh .. + 7)
+      uint4 va[4][2];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          va[dt][ks] = *reinterpret_cast<const uint4*>(sb + KBUF + (32 * dt + n) * VROW + (16 * ks + 8 * hh) * 2);
+      if (k0 + KT > key_end) {                           // zero V rows of keys past the end (NaN poison)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int kb = k0 + 16 * ks + 8 * hh;
+          uint32_t msk[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            msk[e] = (kb + 2 * e < key_end ? 0x0000FFFFu : 0u) | (kb + 2 * e + 1 < key_end ? 0xFFFF0000u : 0u);
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            va[dt][ks].x &= msk[0]; va[dt][ks].y &= msk[1]; va[dt][ks].z &= msk[2]; va[dt][ks].w &= msk[3];
+          }
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        o[dt] = mfma32(va[dt][0], pb[0], o[dt]);
+        o[dt] = mfma32(va[dt][1], pb[1], o[dt]);
+      }
     }
+    // every wave has finished reading buffer (kt + 1) & 1 (at the previous
+    // tile's barrier), so it can take the next tile now
+    stage_store((kt + 1) & 1);
+    __syncthreads();
   }
 
   // ---- normalise and store: accumulator r of d-tile dt is dim 32dt + 8(r/4) + 4hh + (r%4)
@@ -209,7 +273,8 @@ hipError_t launch_prefill_chunk(const PrefillArgs& a0, int block_size, int group
   if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
 #define PA_PF(b, g) \
   if (block_size == b && group == g) { \
-    hipLaunchKernelGGL((prefill_kernel<b, g>), dim3(uint32_t(wgs)), dim3(256), 0, s, a); \
+    hipLaunchKernelGGL((prefill_kernel<b, g>), dim3(uint32_t(wgs)), dim3(256), 0, s, a, a.block_table, a.cu_q_lens, \
+                       a.seq_lens); \
     return hipGetLastError(); \
   }
   PA_PF(16, 1) PA_PF(16, 2) PA_PF(16, 4) PA_PF(16, 8)
