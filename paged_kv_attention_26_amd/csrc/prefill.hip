@@ -26,7 +26,9 @@
 //    operands, without a pass through LDS.  V is stored transposed per
 //    block, so its A operand (8 consecutive keys of one head dimension) is
 //    one 16-byte load.
-//  * Online softmax in base 2 with the scale folded into exp2's argument;
+//  * Online softmax in base 2 with the scale folded into exp2's argument
+//    (the hardware v_exp_f32: arguments are <= 0, results that would be
+//    denormal flush to zero, far below bf16 resolution of the sum);
 //    O^T is rescaled only when some column's running max grows.
 //  * The causal mask is applied only on key tiles that reach the diagonal;
 //    keys past the sequence are masked by select and their V rows zeroed,
@@ -50,6 +52,9 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const
 // MFMA row m of a key tile holds key swap_bits_2_3(m) (an involution).
 __device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
+// Sequences of a launch are ordered by work when there are at most this many.
+constexpr int kPrefillSortMax = 256;
+
 template <int B, int G>
 __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a, const int32_t* __restrict__ block_table,
                                                         const int32_t* __restrict__ cu_q_lens,
@@ -70,14 +75,36 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a, const in
   const int n = lane & 31;               // query column / operand row
   const int Hkv = a.num_kv_heads, Hq = a.num_q_heads;
 
-  // ---- workgroup -> (sequence, kv head, group of 4 column tiles), XCD-aware
+  // ---- workgroup -> (sequence, kv head, group of 4 column tiles), XCD-aware:
+  // the workgroups of one (sequence, kv head) run on one XCD (id mod 8) and
+  // share its L2.  Sequences are taken heaviest first (work ~ q_len * (2P +
+  // q_len)), so that the longest chains of key tiles start first.
   const int id = blockIdx.x;
   const int xcd = id & 7;
   const int k8 = id >> 3;
-  const int pair = (k8 / a.wg_per_pair) * 8 + xcd;
-  if (pair >= a.num_seqs * Hkv) return;                  // whole workgroup
+  const int pair = (k8 / a.wg_per_pair) * 8 + xcd;       // rank of the (sequence, kv head)
+  const int S = a.num_seqs;
+  if (pair >= S * Hkv) return;                           // whole workgroup
   const int grp = k8 % a.wg_per_pair;
-  const int seq = pair / Hkv, kvh = pair - seq * Hkv;
+  int seq = pair / Hkv;
+  const int kvh = pair - seq * Hkv;
+  if (S <= kPrefillSortMax) {
+    __shared__ float s_work[kPrefillSortMax];
+    __shared__ int s_order[kPrefillSortMax];
+    for (int i = tid; i < S; i += 256) {
+      const float ql = float(cu_q_lens[i + 1] - cu_q_lens[i]);
+      s_work[i] = ql * (2.f * (float(seq_lens[i]) - ql) + ql);
+    }
+    __syncthreads();
+    for (int i = tid; i < S; i += 256) {
+      const float wi = s_work[i];
+      int rank = 0;
+      for (int j = 0; j < S; ++j) rank += (s_work[j] > wi) || (s_work[j] == wi && j < i);
+      s_order[rank] = i;
+    }
+    __syncthreads();
+    seq = s_order[seq];
+  }
   const int q0 = cu_q_lens[seq];
   const int q_len = cu_q_lens[seq + 1] - q0;
   const int total = seq_lens[seq];
@@ -113,27 +140,31 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a, const in
   // range re-read its last key (their scores are masked, their V zeroed).
   const int kr0 = tid >> 4, kcc = tid & 15;
   const int vd0 = tid >> 2, vkc = tid & 3;
-  uint4 kst0, kst1, vst0, vst1;
-  auto stage_load = [&](int kt, int id0, int id1) __attribute__((always_inline)) {
-    const int k0 = kt * KT;
-    const int b0 = k0 / B;
-    const int key0 = min(k0 + kr0, kmax), key1 = min(k0 + kr0 + 16, kmax);
-    const int bk0 = key0 / B == b0 ? id0 : id1, bk1 = key1 / B == b0 ? id0 : id1;
-    kst0 = *reinterpret_cast<const uint4*>(kpool + ((size_t(bk0) * Hkv + kvh) * B + key0 % B) * (D * 2) + kcc * 16);
-    kst1 = *reinterpret_cast<const uint4*>(kpool + ((size_t(bk1) * Hkv + kvh) * B + key1 % B) * (D * 2) + kcc * 16);
-    const int kb = min(k0 + 8 * vkc, kmax & ~7);
-    const int bv = kb / B == b0 ? id0 : id1;
-    const char* vsrc = vpool + ((size_t(bv) * Hkv + kvh) * D + vd0) * (B * 2) + (kb % B) * 2;
-    vst0 = *reinterpret_cast<const uint4*>(vsrc);
-    vst1 = *reinterpret_cast<const uint4*>(vsrc + 64 * (B * 2));
-  };
-  auto stage_store = [&](int buf) __attribute__((always_inline)) {
-    char* sb = smem[buf];
-    *reinterpret_cast<uint4*>(sb + kr0 * KROW + kcc * 16) = kst0;
-    *reinterpret_cast<uint4*>(sb + (kr0 + 16) * KROW + kcc * 16) = kst1;
-    *reinterpret_cast<uint4*>(sb + KBUF + vd0 * VROW + vkc * 16) = vst0;
-    *reinterpret_cast<uint4*>(sb + KBUF + (vd0 + 64) * VROW + vkc * 16) = vst1;
-  };
+  // (macros over plain variables: two staging sets, kept in registers)
+#define PA_STAGE_LOAD(P, KT_, ID0, ID1)                                                                           \
+  do {                                                                                                        \
+    const int k0_ = (KT_) * KT;                                                                               \
+    const int b0_ = k0_ / B;                                                                                  \
+    const int key0_ = min(k0_ + kr0, kmax), key1_ = min(k0_ + kr0 + 16, kmax);                                \
+    const int bk0_ = key0_ / B == b0_ ? (ID0) : (ID1), bk1_ = key1_ / B == b0_ ? (ID0) : (ID1);              \
+    P##k0 = *reinterpret_cast<const uint4*>(kpool + ((size_t(bk0_) * Hkv + kvh) * B + key0_ % B) * (D * 2) +  \
+                                            kcc * 16);                                                        \
+    P##k1 = *reinterpret_cast<const uint4*>(kpool + ((size_t(bk1_) * Hkv + kvh) * B + key1_ % B) * (D * 2) +  \
+                                            kcc * 16);                                                        \
+    const int kb_ = min(k0_ + 8 * vkc, kmax & ~7);                                                            \
+    const int bv_ = kb_ / B == b0_ ? (ID0) : (ID1);                                                           \
+    const char* vsrc_ = vpool + ((size_t(bv_) * Hkv + kvh) * D + vd0) * (B * 2) + (kb_ % B) * 2;              \
+    P##v0 = *reinterpret_cast<const uint4*>(vsrc_);                                                           \
+    P##v1 = *reinterpret_cast<const uint4*>(vsrc_ + 64 * (B * 2));                                            \
+  } while (0)
+#define PA_STAGE_STORE(P, BUF)                                                                                \
+  do {                                                                                                        \
+    char* sb_ = smem[BUF];                                                                                    \
+    *reinterpret_cast<uint4*>(sb_ + kr0 * KROW + kcc * 16) = P##k0;                                           \
+    *reinterpret_cast<uint4*>(sb_ + (kr0 + 16) * KROW + kcc * 16) = P##k1;                                    \
+    *reinterpret_cast<uint4*>(sb_ + KBUF + vd0 * VROW + vkc * 16) = P##v0;                                    \
+    *reinterpret_cast<uint4*>(sb_ + KBUF + (vd0 + 64) * VROW + vkc * 16) = P##v1;                             \
+  } while (0)
   // block ids of a tile's (at most two) blocks, read through the scalar cache
   auto tile_ids = [&](int kt, int& id0, int& id1) __attribute__((always_inline)) {
     const int b0 = kt * KT / B;
@@ -157,19 +188,11 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a, const in
   const int my_key = swap23(n);                          // key of MFMA row n within a tile
   const int first_row_pos = P + qt * QT;                 // smallest query position of the tile
 
-  int id0, id1, nid0, nid1;
-  tile_ids(0, id0, id1);
-  stage_load(0, id0, id1);
-  tile_ids(min(1, n_tiles_wg - 1), nid0, nid1);
-  stage_store(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < n_tiles_wg; ++kt) {
-    // next tile's global loads fly during this tile's MFMAs (the last tile re-reads itself)
-    stage_load(min(kt + 1, n_tiles_wg - 1), nid0, nid1);
-    tile_ids(min(kt + 2, n_tiles_wg - 1), nid0, nid1);
-    const char* sb = smem[kt & 1];
-
+  // Two staging register sets: a tile's global loads are issued two tiles
+  // before its own MFMAs and written to LDS one tile before them, so about
+  // two tiles of MFMA work cover each load's latency.  Tiles past the last
+  // re-read the last one.
+  auto compute_tile = [&](int kt, const char* sb) __attribute__((always_inline)) {
     if (kt < n_tiles) {
       const int k0 = kt * KT;
       // ---- S^T = K Q^T  (A: lane row n = key k0 + my_key, dims 16s + 8hh)
@@ -194,7 +217,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a, const in
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       const float m_new = fmaxf(m_run, mt);
       if (__any(m_new > m_run)) {
-        const float al = exp2f((m_run - m_new) * c);
+        const float al = __builtin_amdgcn_exp2f((m_run - m_new) * c);
         l_run *= al;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
@@ -206,7 +229,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a, const in
       float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = exp2f(fmaf(sc[r], c, -mc));
+        p[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -mc));
         l_run += p[r];
       }
       // P^T operands: key slice ks takes accumulators 8ks .. 8ks + 7 (keys k0 + 16ks + 8hh + 0..7)
@@ -242,11 +265,33 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a, const in
         o[dt] = mfma32(va[dt][1], pb[1], o[dt]);
       }
     }
-    // every wave has finished reading buffer (kt + 1) & 1 (at the previous
-    // tile's barrier), so it can take the next tile now
-    stage_store((kt + 1) & 1);
+  };
+
+  const int last = n_tiles_wg - 1;
+  uint4 sa_k0, sa_k1, sa_v0, sa_v1, sb_k0, sb_k1, sb_v0, sb_v1;
+  int j0, j1;
+  tile_ids(0, j0, j1);
+  PA_STAGE_LOAD(sa_, 0, j0, j1);
+  tile_ids(min(1, last), j0, j1);
+  PA_STAGE_LOAD(sb_, min(1, last), j0, j1);
+  tile_ids(min(2, last), j0, j1);
+  PA_STAGE_STORE(sa_, 0);
+  __syncthreads();
+  for (int kt = 0; kt < n_tiles_wg; kt += 2) {
+    PA_STAGE_LOAD(sa_, min(kt + 2, last), j0, j1);          // tile kt + 2, stored at the odd half
+    tile_ids(min(kt + 3, last), j0, j1);
+    compute_tile(kt, smem[0]);
+    PA_STAGE_STORE(sb_, 1);                                  // tile kt + 1
+    __syncthreads();
+    if (kt + 1 >= n_tiles_wg) break;
+    PA_STAGE_LOAD(sb_, min(kt + 3, last), j0, j1);          // tile kt + 3, stored at the next even half
+    tile_ids(min(kt + 4, last), j0, j1);
+    compute_tile(kt + 1, smem[1]);
+    PA_STAGE_STORE(sa_, 0);                                  // tile kt + 2
     __syncthreads();
   }
+#undef PA_STAGE_LOAD
+#undef PA_STAGE_STORE
 
   // ---- normalise and store: accumulator r of d-tile dt is dim 32dt + 8(r/4) + 4hh + (r%4)
   const float l = l_run + __shfl_xor(l_run, 32);
