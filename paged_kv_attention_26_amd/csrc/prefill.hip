@@ -9,13 +9,14 @@
 //
 // How (QK^T and PV are dense contractions, so they run on MFMA; bf16 in,
 // fp32 accumulate):
-//  * A wave owns 32 query rows of one query head; the four waves of a
-//    workgroup share a kv head (the G heads of a group, or neighbouring query
-//    tiles).  The workgroup stages each 32-key K / V^T tile once into LDS
-//    (rows padded so that the MFMA operand reads are free of bank conflicts),
+//  * A wave owns 32 query rows of one query head; the eight waves of a
+//    workgroup share a kv head (two query tiles of the G = 4 heads of a
+//    group, or more tiles of fewer heads).  The workgroup stages each 32-key K / V^T tile once into LDS
+//    (K chunks XOR-swizzled, V^T rows padded, so that the MFMA operand reads
+//    are free of bank conflicts),
 //    double-buffered: the next tile's global loads fly while the current
 //    tile's MFMAs run, one barrier per tile.  Block ids come through the
-//    scalar cache.  Two workgroups fit on a CU.
+//    scalar cache.  Two waves share each SIMD.
 //  * Scores are formed transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 //    (keys are MFMA rows, queries columns): every lane then owns one query
 //    column, and the softmax statistics and the rescaling of O^T stay in the
@@ -52,17 +53,26 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const
 // MFMA row m of a key tile holds key swap_bits_2_3(m) (an involution).
 __device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
+// LDS swizzle of a key row's 16-byte chunks: chunk c of key row r sits at
+// c ^ kswz(r).  Lane n reads key row swap23(n), so the lanes of any group of
+// 8 or 16 read chunk c ^ (n & 15): distinct bank groups, no conflicts.
+__device__ __forceinline__ int kswz(int r) { return swap23(r) & 15; }
+
 // Sequences of a launch are ordered by work when there are at most this many.
 constexpr int kPrefillSortMax = 256;
 
+// Waves per workgroup: two query tiles of four heads (or more tiles of
+// fewer heads) share every staged K / V tile.
+constexpr int kPrefillWaves = 8;
+
 template <int B, int G>
-__global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a, const int32_t* __restrict__ block_table,
+__global__ void __launch_bounds__(kPrefillWaves * 64) prefill_kernel(PrefillArgs a, const int32_t* __restrict__ block_table,
                                                         const int32_t* __restrict__ cu_q_lens,
                                                         const int32_t* __restrict__ seq_lens) {
   constexpr int D = 128;
   constexpr int QT = 32;                 // query rows per wave
   constexpr int KT = 32;                 // keys per tile
-  constexpr int KROW = D * 2 + 16;       // LDS bytes per key row (16 bytes of padding: conflict-free operand reads)
+  constexpr int KROW = D * 2;            // LDS bytes per key row; 16-byte chunks XOR-swizzled by kswz(row)
   constexpr int VROW = KT * 2 + 16;      // LDS bytes per head-dim row of the transposed value tile
   constexpr int KBUF = KT * KROW;
   constexpr int BUF = KBUF + D * VROW;
@@ -91,12 +101,12 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a, const in
   if (S <= kPrefillSortMax) {
     __shared__ float s_work[kPrefillSortMax];
     __shared__ int s_order[kPrefillSortMax];
-    for (int i = tid; i < S; i += 256) {
+    for (int i = tid; i < S; i += kPrefillWaves * 64) {
       const float ql = float(cu_q_lens[i + 1] - cu_q_lens[i]);
       s_work[i] = ql * (2.f * (float(seq_lens[i]) - ql) + ql);
     }
     __syncthreads();
-    for (int i = tid; i < S; i += 256) {
+    for (int i = tid; i < S; i += kPrefillWaves * 64) {
       const float wi = s_work[i];
       int rank = 0;
       for (int j = 0; j < S; ++j) rank += (s_work[j] > wi) || (s_work[j] == wi && j < i);
@@ -110,17 +120,19 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a, const in
   const int total = seq_lens[seq];
   const int P = total - q_len;
   // wave w serves query head kvh * G + (col % G) on query tile qt (heavy, late tiles first)
-  auto tile_of = [&](int wv) { return a.num_qtiles - 1 - (grp * 4 + wv) / G; };
+  auto tile_of = [&](int wv) { return a.num_qtiles - 1 - (grp * kPrefillWaves + wv) / G; };
   auto key_end_of = [&](int wv) {                        // keys the wave's last row needs; 0 if idle
     const int t = tile_of(wv);
     return (t >= 0 && t * QT < q_len) ? P + min(q_len, (t + 1) * QT) : 0;
   };
   // the workgroup streams the keys any of its waves needs
-  const int key_end_wg = max(max(key_end_of(0), key_end_of(1)), max(key_end_of(2), key_end_of(3)));
+  int key_end_wg = 0;
+#pragma unroll
+  for (int wv = 0; wv < kPrefillWaves; ++wv) key_end_wg = max(key_end_wg, key_end_of(wv));
   if (key_end_wg <= 0) return;                           // whole workgroup
   const int n_tiles_wg = (key_end_wg + KT - 1) / KT;
   const int kmax = key_end_wg - 1;
-  const int col = grp * 4 + w;
+  const int col = grp * kPrefillWaves + w;
   const int h_local = col % G;
   const int qt = tile_of(w);
   const int key_end = key_end_of(w);
@@ -134,36 +146,32 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a, const in
   const char* vpool = static_cast<const char*>(a.v_cache);
   const float c = a.scale_log2;
 
-  // ---- staging of one tile by the whole workgroup: each thread moves two
-  // 16-byte chunks of K (rows kr0, kr0 + 16; column chunk kcc) and two of V^T
-  // (head dims vd0, vd0 + 64; 8-key group vkc).  Keys past the workgroup's
-  // range re-read its last key (their scores are masked, their V zeroed).
-  const int kr0 = tid >> 4, kcc = tid & 15;
-  const int vd0 = tid >> 2, vkc = tid & 3;
+  // ---- staging of one tile by the whole workgroup: each thread moves one
+  // 16-byte chunk of K (row kr, column chunk kcc) and one of V^T (head dim
+  // vd, 8-key group vkc).  Keys past the workgroup's range re-read its last
+  // key (their scores are masked, their V zeroed).
+  static_assert(kPrefillWaves * 64 == KT * 16 && kPrefillWaves * 64 == D * 4, "one chunk of K and V per thread");
+  const int kr = tid >> 4, kcc = tid & 15;
+  const int vd = tid >> 2, vkc = tid & 3;
   // (macros over plain variables: two staging sets, kept in registers)
 #define PA_STAGE_LOAD(P, KT_, ID0, ID1)                                                                           \
   do {                                                                                                        \
     const int k0_ = (KT_) * KT;                                                                               \
     const int b0_ = k0_ / B;                                                                                  \
-    const int key0_ = min(k0_ + kr0, kmax), key1_ = min(k0_ + kr0 + 16, kmax);                                \
-    const int bk0_ = key0_ / B == b0_ ? (ID0) : (ID1), bk1_ = key1_ / B == b0_ ? (ID0) : (ID1);              \
-    P##k0 = *reinterpret_cast<const uint4*>(kpool + ((size_t(bk0_) * Hkv + kvh) * B + key0_ % B) * (D * 2) +  \
-                                            kcc * 16);                                                        \
-    P##k1 = *reinterpret_cast<const uint4*>(kpool + ((size_t(bk1_) * Hkv + kvh) * B + key1_ % B) * (D * 2) +  \
-                                            kcc * 16);                                                        \
+    const int key_ = min(k0_ + kr, kmax);                                                                     \
+    const int bk_ = key_ / B == b0_ ? (ID0) : (ID1);                                                          \
+    P##k = *reinterpret_cast<const uint4*>(kpool + ((size_t(bk_) * Hkv + kvh) * B + key_ % B) * (D * 2) +     \
+                                           kcc * 16);                                                         \
     const int kb_ = min(k0_ + 8 * vkc, kmax & ~7);                                                            \
     const int bv_ = kb_ / B == b0_ ? (ID0) : (ID1);                                                           \
-    const char* vsrc_ = vpool + ((size_t(bv_) * Hkv + kvh) * D + vd0) * (B * 2) + (kb_ % B) * 2;              \
-    P##v0 = *reinterpret_cast<const uint4*>(vsrc_);                                                           \
-    P##v1 = *reinterpret_cast<const uint4*>(vsrc_ + 64 * (B * 2));                                            \
+    P##v = *reinterpret_cast<const uint4*>(vpool + ((size_t(bv_) * Hkv + kvh) * D + vd) * (B * 2) +           \
+                                           (kb_ % B) * 2);                                                    \
   } while (0)
 #define PA_STAGE_STORE(P, BUF)                                                                                \
   do {                                                                                                        \
     char* sb_ = smem[BUF];                                                                                    \
-    *reinterpret_cast<uint4*>(sb_ + kr0 * KROW + kcc * 16) = P##k0;                                           \
-    *reinterpret_cast<uint4*>(sb_ + (kr0 + 16) * KROW + kcc * 16) = P##k1;                                    \
-    *reinterpret_cast<uint4*>(sb_ + KBUF + vd0 * VROW + vkc * 16) = P##v0;                                    \
-    *reinterpret_cast<uint4*>(sb_ + KBUF + (vd0 + 64) * VROW + vkc * 16) = P##v1;                             \
+    *reinterpret_cast<uint4*>(sb_ + kr * KROW + (kcc ^ kswz(kr)) * 16) = P##k;                                \
+    *reinterpret_cast<uint4*>(sb_ + KBUF + vd * VROW + vkc * 16) = P##v;                                      \
   } while (0)
   // block ids of a tile's (at most two) blocks, read through the scalar cache
   auto tile_ids = [&](int kt, int& id0, int& id1) __attribute__((always_inline)) {
@@ -198,7 +206,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a, const in
       // ---- S^T = K Q^T  (A: lane row n = key k0 + my_key, dims 16s + 8hh)
       uint4 ka[8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) ka[s] = *reinterpret_cast<const uint4*>(sb + my_key * KROW + (16 * s + 8 * hh) * 2);
+      for (int s = 0; s < 8; ++s)
+        ka[s] = *reinterpret_cast<const uint4*>(sb + my_key * KROW + ((2 * s + hh) ^ kswz(my_key)) * 16);
       f32x16_t sc = f32x16_t{};
 #pragma unroll
       for (int st = 0; st < 8; ++st) sc = mfma32(ka[st], qb[st], sc);
@@ -268,7 +277,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a, const in
   };
 
   const int last = n_tiles_wg - 1;
-  uint4 sa_k0, sa_k1, sa_v0, sa_v1, sb_k0, sb_k1, sb_v0, sb_v1;
+  uint4 sa_k, sa_v, sb_k, sb_v;
   int j0, j1;
   tile_ids(0, j0, j1);
   PA_STAGE_LOAD(sa_, 0, j0, j1);
@@ -311,15 +320,15 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a, const in
 hipError_t launch_prefill_chunk(const PrefillArgs& a0, int block_size, int group, hipStream_t s) {
   PrefillArgs a = a0;
   a.num_qtiles = (a.max_q_len + 31) / 32;
-  a.wg_per_pair = (group * a.num_qtiles + 3) / 4;
+  a.wg_per_pair = (group * a.num_qtiles + kPrefillWaves - 1) / kPrefillWaves;
   const int64_t pairs = int64_t(a.num_seqs) * a.num_kv_heads;
   const int64_t wgs = ((pairs + 7) / 8) * 8 * a.wg_per_pair;
   if (wgs == 0) return hipSuccess;
   if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
 #define PA_PF(b, g) \
   if (block_size == b && group == g) { \
-    hipLaunchKernelGGL((prefill_kernel<b, g>), dim3(uint32_t(wgs)), dim3(256), 0, s, a, a.block_table, a.cu_q_lens, \
-                       a.seq_lens); \
+    hipLaunchKernelGGL((prefill_kernel<b, g>), dim3(uint32_t(wgs)), dim3(kPrefillWaves * 64), 0, s, a, a.block_table, \
+                       a.cu_q_lens, a.seq_lens); \
     return hipGetLastError(); \
   }
   PA_PF(16, 1) PA_PF(16, 2) PA_PF(16, 4) PA_PF(16, 8)
