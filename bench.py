@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = library default)")
     ap.add_argument("--no-extras", action="store_true", help="skip the secondary measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--only-extra", choices=EXTRA_GROUPS, default=None,
+                    help="run only this group of secondary measurements and print them (for profiling)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB device buffer 4 times (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -84,11 +86,15 @@ def timed_calls(fn, reps, warm=3):
     return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
 
 
-def extras(pa, runner, W, torch):
-    """Secondary measurements: long-context decode at block 16 and 32, the
-    mixed chunked-prefill batch, the fp8 fork decode, bulk store."""
+EXTRA_GROUPS = ("long_context", "mixed", "fork")
+
+
+def extras(pa, runner, W, torch, groups=EXTRA_GROUPS):
+    """Secondary measurements: long-context decode at block 16 and 32 with
+    the bulk store ("long_context"), the mixed chunked-prefill batch's store,
+    decode and prefill ("mixed"), the fp8 fork decode ("fork")."""
     out = {}
-    for B in (16, 32):
+    for B in ((16, 32) if "long_context" in groups else ()):
         b = W.config3(B)
         g = runner.prepare(b)
         runner.store_step(g)
@@ -107,13 +113,29 @@ def extras(pa, runner, W, torch):
                                          frac=round(moved / med / 1e6 / HBM_PEAK_GBS, 4))
         del g
         torch.cuda.empty_cache()
+    if "mixed" in groups:
+        mixed_batch(pa, runner, W, out)
+    if "fork" in groups:
+        fb = W.config5()
+        gf = runner.run_fork(fb)
+        med, _, _ = timed_calls(lambda: runner.fork_decode(gf), 20)
+        lens = [gf.bm.seq_len(x) for x in gf.beams]
+        byt = kv_bytes(lens, fb.num_kv_heads, fb.head_dim, 1)
+        out["fork_fp8_decode"] = dict(GBps_logical=round(byt / med / 1e6, 1), ms=round(med, 4),
+                                      note="cache resident: 8 beams share the prompt blocks")
+    return out
+
+
+def mixed_batch(pa, runner, W, out):
+    """Mixed chunked-prefill batch: the step's store, the decode of its 64
+    sequences and the prefill of its 8 chunks of 512."""
     b = W.config4()
     g = runner.prepare(b)
     med, _, _ = timed_calls(lambda: runner.store_step(g), 20)
     T = g.step_slots.numel()
     out["mixed_store"] = dict(GBps=round(T * b.num_kv_heads * b.head_dim * 8 / med / 1e6, 1), ms=round(med, 4))
     runner.store_step(g)
-    ws = pa.decode_workspace(len(g.dec["idx"]), b.num_q_heads, b.head_dim, g.dec["max_len"], 512)
+    ws = pa.decode_workspace(len(g.dec["idx"]), b.num_q_heads, b.head_dim, g.dec["max_len"], 0)
     med, _, _ = timed_calls(lambda: runner.decode_step(g, workspace=ws), 20)
     byt = kv_bytes(g.dec["host_lens"], b.num_kv_heads, b.head_dim, 2)
     out["mixed_decode"] = dict(GBps=round(byt / med / 1e6, 1), ms=round(med, 4))
@@ -123,15 +145,6 @@ def extras(pa, runner, W, torch):
         fl += 4 * b.head_dim * b.num_q_heads * (int(n) * int(P) + int(n) * (int(n) + 1) // 2)
     out["mixed_prefill_chunk"] = dict(TFLOPs=round(fl / med / 1e9, 1), ms=round(med, 4),
                                       frac=round(fl / med / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4), flops=fl)
-    del g
-    fb = W.config5()
-    gf = runner.run_fork(fb)
-    med, _, _ = timed_calls(lambda: runner.fork_decode(gf), 20)
-    lens = [gf.bm.seq_len(x) for x in gf.beams]
-    byt = kv_bytes(lens, fb.num_kv_heads, fb.head_dim, 1)
-    out["fork_fp8_decode"] = dict(GBps_logical=round(byt / med / 1e6, 1), ms=round(med, 4),
-                                  note="cache resident: 8 beams share the prompt blocks")
-    return out
 
 
 def cpu_baseline(batch, budget_s=10.0):
@@ -185,6 +198,9 @@ def main():
         return
     import workloads as W
     from paged_kv_attention_26_amd import binding as pa, runner
+    if args.only_extra:
+        print(json.dumps({"extras": extras(pa, runner, W, torch, (args.only_extra,))}), flush=True)
+        return
 
     base = W.config2()
     lens_all = base.total_lens
