@@ -91,15 +91,16 @@ EXTRA_GROUPS = ("long_context", "mixed", "fork")
 
 def extras(pa, runner, W, torch, groups=EXTRA_GROUPS):
     """Secondary measurements: long-context decode at block 16 and 32 with
-    the bulk store ("long_context"), the mixed chunked-prefill batch's store,
+    the bulk store and a bulk block copy ("long_context"), the mixed chunked-prefill batch's store,
     decode and prefill ("mixed"), the fp8 fork decode ("fork")."""
     out = {}
     for B in ((16, 32) if "long_context" in groups else ()):
         b = W.config3(B)
         g = runner.prepare(b)
         runner.store_step(g)
-        ws = pa.decode_workspace(len(g.dec["idx"]), b.num_q_heads, b.head_dim, g.dec["max_len"], 0)
-        med, p10, p90 = timed_calls(lambda: runner.decode_step(g, partition_tokens=0, workspace=ws), 20)
+        # the workload's own split: partitions of 512 tokens
+        ws = pa.decode_workspace(len(g.dec["idx"]), b.num_q_heads, b.head_dim, g.dec["max_len"], 512)
+        med, p10, p90 = timed_calls(lambda: runner.decode_step(g, partition_tokens=512, workspace=ws), 20)
         byt = kv_bytes(g.dec["host_lens"], b.num_kv_heads, b.head_dim, 2)
         out[f"long_context_decode_b{B}"] = dict(GBps=round(byt / med / 1e6, 1), ms=round(med, 4),
                                                 p10_ms=round(p10, 4), p90_ms=round(p90, 4),
@@ -111,6 +112,16 @@ def extras(pa, runner, W, torch, groups=EXTRA_GROUPS):
             moved = T * b.num_kv_heads * b.head_dim * 2 * (2 + 2) + 4 * T
             out["bulk_store_b16"] = dict(GBps=round(moved / med / 1e6, 1), ms=round(med, 3), tokens=T,
                                          frac=round(moved / med / 1e6 / HBM_PEAK_GBS, 4))
+            # bulk copy-on-write: every free block of the pool receives a copy of a used one
+            used = sorted({blk for row in g.tables for blk in row})
+            free = sorted(set(range(b.num_blocks)) - set(used))
+            n = min(len(used), len(free))
+            pairs = torch.tensor(np.stack([np.array(used[:n]), np.array(free[:n])], 1), dtype=torch.int32,
+                                 device="cuda")
+            med, _, _ = timed_calls(lambda: pa.copy_blocks(g.cache, pairs), 10, warm=2)
+            moved = n * 2 * 2 * b.num_kv_heads * B * b.head_dim * 2
+            out["bulk_copy_b16"] = dict(GBps=round(moved / med / 1e6, 1), ms=round(med, 3), pairs=n,
+                                        frac=round(moved / med / 1e6 / HBM_PEAK_GBS, 4))
         del g
         torch.cuda.empty_cache()
     if "mixed" in groups:

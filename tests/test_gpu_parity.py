@@ -99,7 +99,7 @@ def test_store_is_bit_exact_over_the_whole_pool(name):
 
 
 @pytest.mark.parametrize("name", list(SMALL))
-@pytest.mark.parametrize("part", [0, 64, 128])
+@pytest.mark.parametrize("part", [0, 64, 128, 512])
 def test_decode_matches_oracle(name, part):
     from paged_kv_attention_26_amd import runner
     say(f"[gpu] decode {name} partition {part}")
