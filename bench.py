@@ -86,13 +86,14 @@ def timed_calls(fn, reps, warm=3):
     return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
 
 
-EXTRA_GROUPS = ("long_context", "mixed", "fork")
+EXTRA_GROUPS = ("long_context", "mixed", "fork", "verify")
 
 
 def extras(pa, runner, W, torch, groups=EXTRA_GROUPS):
     """Secondary measurements: long-context decode at block 16 and 32 with
     the bulk store and a bulk block copy ("long_context"), the mixed chunked-prefill batch's store,
-    decode and prefill ("mixed"), the fp8 fork decode ("fork")."""
+    decode and prefill ("mixed"), the fp8 fork decode ("fork"), speculative
+    verification of 4 draft tokens on the Qwen3-8B layer ("verify")."""
     out = {}
     for B in ((16, 32) if "long_context" in groups else ()):
         b = W.config3(B)
@@ -126,6 +127,19 @@ def extras(pa, runner, W, torch, groups=EXTRA_GROUPS):
         torch.cuda.empty_cache()
     if "mixed" in groups:
         mixed_batch(pa, runner, W, out)
+    if "verify" in groups:
+        b = W.verify_batch()
+        g = runner.prepare(b)
+        runner.store_step(g)
+        med, p10, p90 = timed_calls(lambda: runner.chunk_step(g), 20)
+        tl, ql = g.chunk["host_prefix"] + g.chunk["host_q"], g.chunk["host_q"]
+        byt = kv_bytes(tl, b.num_kv_heads, b.head_dim, 2)
+        fl = sum(4 * b.head_dim * b.num_q_heads * (int(n) * int(P) + int(n) * (int(n) + 1) // 2)
+                 for P, n in zip(g.chunk["host_prefix"], ql))
+        out["verify_k4"] = dict(GBps=round(byt / med / 1e6, 1), frac=round(byt / med / 1e6 / HBM_PEAK_GBS, 4),
+                                TFLOPs=round(fl / med / 1e9, 1), ms=round(med, 4), p10_ms=round(p10, 4),
+                                p90_ms=round(p90, 4), kv_bytes=byt, tokens=int(np.sum(tl)))
+        del g
     if "fork" in groups:
         fb = W.config5()
         gf = runner.run_fork(fb)

@@ -23,6 +23,7 @@ SOURCES = [
     "decode_f32.hip",
     "decode_bf16.hip",
     "decode_fp8.hip",
+    "verify.hip",
     "prefill.hip",
 ]
 

@@ -79,5 +79,7 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_kind, int head_dim, int blo
                          int64_t upper_units, hipStream_t s);
 // bf16 cache, head_dim 128; hipErrorInvalidValue for an uncompiled combination.
 hipError_t launch_prefill_chunk(const PrefillArgs& a, int block_size, int group, hipStream_t s);
+// Chunks of at most 32 / group tokens; called by launch_prefill_chunk.
+hipError_t launch_verify_chunk(const PrefillArgs& a, int block_size, int group, hipStream_t s);
 
 }  // namespace pa

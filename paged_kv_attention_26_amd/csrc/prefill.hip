@@ -37,21 +37,11 @@
 //  * Workgroups of one (sequence, kv head) are placed on the same XCD
 //    (workgroup id mod 8), so all query tiles of a sequence share that
 //    XCD's L2 copy of its K/V.
+#include "mfma_attn.h"
 #include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
-                                                 0, 0, 0);
-}
-
-// MFMA row m of a key tile holds key swap_bits_2_3(m) (an involution).
-__device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
 // LDS swizzle of a key row's 16-byte chunks: chunk c of key row r sits at
 // c ^ kswz(r).  Lane n reads key row swap23(n), so the lanes of any group of
@@ -318,6 +308,9 @@ __global__ void __launch_bounds__(kPrefillWaves * 64) prefill_kernel(PrefillArgs
 }
 
 hipError_t launch_prefill_chunk(const PrefillArgs& a0, int block_size, int group, hipStream_t s) {
+  // chunks of at most 32 / G tokens (speculative verification) fill the MFMA
+  // columns with (head, token) pairs instead of 32 rows of one head
+  if (int64_t(a0.max_q_len) * group <= 32) return launch_verify_chunk(a0, block_size, group, s);
   PrefillArgs a = a0;
   a.num_qtiles = (a.max_q_len + 31) / 32;
   a.wg_per_pair = (group * a.num_qtiles + kPrefillWaves - 1) / kPrefillWaves;

@@ -242,6 +242,14 @@ CHUNKS = {
     "g1": lambda: chunk_batch("g1", [17, 300], [45, 70], Hq=8, Hkv=8),
     "g2": lambda: chunk_batch("g2", [17, 300], [45, 70], Hq=16, Hkv=8),
     "g8": lambda: chunk_batch("g8", [17, 300], [45, 70], Hq=32, Hkv=4),
+    # speculative-verification shapes: at most 32 / G tokens per chunk
+    "verify-k4": lambda: chunk_batch("verify-k4", [0, 1, 15, 16, 31, 100, 511, 512, 1023, 4100], [5] * 10),
+    "verify-mixed-b32": lambda: chunk_batch("verify-mixed-b32", [3, 64, 700, 2000, 33], [1, 8, 3, 7, 2], B=32),
+    "verify-long": lambda: chunk_batch("verify-long", [6000, 9000], [5, 8]),
+    "verify-g1": lambda: chunk_batch("verify-g1", [40, 1000], [32, 17], Hq=8, Hkv=8),
+    "verify-g2": lambda: chunk_batch("verify-g2", [40, 1000], [16, 9], Hq=16, Hkv=8),
+    "verify-g8": lambda: chunk_batch("verify-g8", [40, 1000, 0], [4, 3, 4], Hq=32, Hkv=4),
+    "verify-batch-small": lambda: W.verify_batch(small=True),
 }
 
 

@@ -107,6 +107,14 @@ def test_chunk_matches_dense_sdpa():
     assert np.max(np.abs(OS.decode_ref(batch, st) - dense_decode(batch))) < 1e-12
 
 
+def test_verify_chunk_matches_dense_sdpa():
+    """Speculative verification (5-token chunks on paged prefixes) against
+    dense attention with an explicit end-aligned causal mask."""
+    batch = W.verify_batch(small=True)
+    st = OS.build(batch)
+    assert np.max(np.abs(OS.chunk_ref(batch, st) - dense_chunk(batch))) < 1e-12
+
+
 def test_fp8_decode_matches_dense_sdpa():
     """Shared-prefix beams of the small fork config as a plain decode batch."""
     fb = W.config5(small=True)

@@ -228,6 +228,21 @@ def config4(small=False) -> PagedBatch:
                        prior_lens=prior, new_lens=new, is_chunk=is_chunk, rng=rng)
 
 
+def verify_batch(small=False, draft=4) -> PagedBatch:
+    """Speculative verification on the Qwen3-8B decode layer: 32 seqs with a
+    prefix of L ~ U{512..4096} accepted tokens, each appending a chunk of
+    draft + 1 tokens (the last accepted token and the draft), bf16, B 16,
+    pool 1.25x.  The chunk's K/V is stored before attention."""
+    seed = 6 if not small else 106
+    rng = np.random.default_rng(seed)
+    n = 6 if small else 32
+    P = rng.integers(1, 1400, size=n) if small else rng.integers(512, 4097, size=n)
+    return paged_batch("qwen3-8b-verify" if not small else "qwen3-8b-verify-small", seed,
+                       kv_dtype="bf16", io_dtype="bf16", Hq=32, Hkv=8, d=128, B=16,
+                       prior_lens=P, new_lens=np.full(n, draft + 1, np.int64), is_chunk=np.ones(n, bool),
+                       rng=rng)
+
+
 def config5(small=False, literal_fork=False) -> ForkBatch:
     """CoW fork with fp8 KV: a 2048-token prompt plus the parent's first generated
     token (2049 shared tokens, so the tail block is partly filled and shared)
