@@ -309,3 +309,76 @@ def test_prefill_full_mixed_batch_sampled():
         err = np.max(np.abs(out[cu[j]:cu[j + 1]] - ref))
         say(f"      seq {j} (prefix {int(batch.prior_lens[i])}) max abs err {err:.3e}")
         assert err < TOL["bf16"]
+
+
+# ------------------------------------------------ full sizes, bench launch configuration
+def test_decode_full_qwen3_layer():
+    """The Qwen3-8B decode layer at full size (32 seqs, 72k tokens), in the
+    launch configuration the benchmark times (default partition): every
+    sequence against the oracle."""
+    from paged_kv_attention_26_amd import binding as pa, runner
+    say("[gpu] decode full qwen3-8b layer")
+    batch = W.config2()
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    ws = pa.decode_workspace(1, 1, batch.head_dim, 1, 0)
+    got = out_f64(runner.decode_step(g, partition_tokens=0, workspace=ws))
+    torch.cuda.synchronize()
+    err = np.max(np.abs(got - OS.decode_ref(batch, OS.build(batch))))
+    say(f"      max abs err {err:.3e}")
+    assert err < TOL["bf16"]
+
+
+_LONG = {}
+
+
+def _long_context(B):
+    if 16 not in _LONG:
+        _LONG.clear()
+        _LONG[16] = W.config3(16)
+    if B not in _LONG:
+        _LONG[B] = W.config3_at_block(_LONG[16], B)
+    return _LONG[B]
+
+
+@pytest.mark.parametrize("B", [16, 32])
+def test_decode_full_long_context_sampled(B):
+    """Long-context decode at full size (128 seqs, 713k tokens, contexts up
+    to 28k) with 512-token partitions, as benchmarked: the longest, the
+    shortest and six seeded sequences against the oracle one by one."""
+    from oracle import paged
+    from paged_kv_attention_26_amd import binding as pa, runner
+    say(f"[gpu] decode full long context B{B}")
+    batch = _long_context(B)
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    ws = pa.decode_workspace(1, 1, batch.head_dim, 1, 512)
+    got = out_f64(runner.decode_step(g, partition_tokens=512, workspace=ws))
+    torch.cuda.synchronize()
+    del g
+    st = OS.build(batch)
+    lens = batch.total_lens
+    pick = {int(np.argmax(lens)), int(np.argmin(lens))}
+    pick |= set(int(x) for x in np.random.default_rng(7).choice(len(lens), 6, replace=False))
+    for i in sorted(pick):
+        tab = OS.table_array([st.tables[i]], st.pad_block)
+        ref = paged.decode_attention(st.kc, st.vc, "bf16", batch.q_decode[i:i + 1], "bf16", tab, lens[i:i + 1],
+                                     batch.scale)
+        err = np.max(np.abs(got[i:i + 1] - ref))
+        say(f"      seq {i} (L {int(lens[i])}) max abs err {err:.3e}")
+        assert err < TOL["bf16"]
+
+
+def test_verify_full_batch():
+    """Speculative verification at full size (32 seqs, 5-token chunks on
+    prefixes up to 4096): every output against the oracle."""
+    from paged_kv_attention_26_amd import runner
+    say("[gpu] verify full batch")
+    batch = W.verify_batch()
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    got = out_f64(runner.chunk_step(g))
+    torch.cuda.synchronize()
+    err = np.max(np.abs(got - OS.chunk_ref(batch, OS.build(batch))))
+    say(f"      max abs err {err:.3e}")
+    assert err < TOL["bf16"]

@@ -21,6 +21,7 @@ head_dim 128); nothing here depends on model weights.
 """
 from __future__ import annotations
 
+import copy
 import math
 from dataclasses import dataclass, field
 from typing import Optional
@@ -199,13 +200,21 @@ def config3(block_size=16, small=False) -> PagedBatch:
                        is_chunk=np.zeros(len(lens), bool), rng=rng)
     if block_size == 16:
         return base
-    rng2 = np.random.default_rng(seed + 1000)
-    nb = _pool_size(base.total_lens, block_size)
-    base.name = base.name.replace("b16", f"b{block_size}")
-    base.block_size = block_size
-    base.num_blocks = nb
-    base.free_order = rng2.permutation(nb).astype(np.int64)
-    return base
+    return config3_at_block(base, block_size)
+
+
+def config3_at_block(base: PagedBatch, block_size: int) -> PagedBatch:
+    """Config 3's run at another block size: the same lengths and K/V/Q
+    values as ``base`` (the block-16 batch), a new 1.25x pool and permutation
+    drawn from a generator seeded base.seed + 1000."""
+    b = copy.copy(base)
+    rng2 = np.random.default_rng(base.seed + 1000)
+    nb = _pool_size(b.total_lens, block_size)
+    b.name = base.name.replace("b16", f"b{block_size}")
+    b.block_size = block_size
+    b.num_blocks = nb
+    b.free_order = rng2.permutation(nb).astype(np.int64)
+    return b
 
 
 def config4(small=False) -> PagedBatch:
