@@ -170,6 +170,14 @@ def mixed_batch(pa, runner, W, out):
         fl += 4 * b.head_dim * b.num_q_heads * (int(n) * int(P) + int(n) * (int(n) + 1) // 2)
     out["mixed_prefill_chunk"] = dict(TFLOPs=round(fl / med / 1e9, 1), ms=round(med, 4),
                                       frac=round(fl / med / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4), flops=fl)
+    del g
+    # the same chunks over an fp8 e4m3 cache (per-head scales; bf16 matrix cores)
+    b8 = W.config4(kv_dtype="fp8")
+    g8 = runner.prepare(b8)
+    runner.store_step(g8)
+    med, _, _ = timed_calls(lambda: runner.chunk_step(g8), 20)
+    out["mixed_prefill_chunk_fp8"] = dict(TFLOPs=round(fl / med / 1e9, 1), ms=round(med, 4),
+                                          frac=round(fl / med / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4))
 
 
 def cpu_baseline(batch, budget_s=10.0):

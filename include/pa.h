@@ -171,8 +171,14 @@ int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* ou
  *   max_q_len, max_seq_len : host upper bounds (size the launch)
  * scale must be finite and > 0.
  * QK^T and PV run on bf16 matrix cores with fp32 accumulation; the
- * probabilities are rounded to bf16 for PV.  Supported: BF16 cache,
- * head_dim 128. */
+ * probabilities are rounded to bf16 for PV.  Supported: BF16 or FP8_E4M3
+ * cache (q and out BF16 either way; an fp8 code of kv head h stands for
+ * code * k_scale[h] or code * v_scale[h], converted to bf16 exactly, the
+ * scales applied outside the contraction), head_dim 128.
+ * Chunks of at most 32 / (num_q_heads / num_kv_heads) tokens -- the shape of
+ * speculative-decoding verification, k draft tokens plus one -- run on a
+ * kernel whose matrix-core columns are the (query head, token) pairs of a
+ * kv head (serving-stack page, speculative decoding). */
 int pa_prefill_chunk(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* out,
                      int32_t out_dtype, int32_t num_seqs, int32_t num_q_heads, float scale,
                      const int32_t* cu_q_lens, const int32_t* seq_lens, const int32_t* block_table,

@@ -219,7 +219,8 @@ int pa_prefill_chunk(const pa_kv_cache* cache, const void* q, int32_t q_dtype, v
                 cache->num_kv_heads);
   const int G = num_q_heads / cache->num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return fail(PA_ERR_UNSUPPORTED, "query group %d not in {1,2,4,8}", G);
-  if (cache->dtype != PA_BF16) return fail(PA_ERR_DTYPE, "pa_prefill_chunk needs a bf16 cache");
+  if (cache->dtype != PA_BF16 && cache->dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_DTYPE, "pa_prefill_chunk needs a bf16 or fp8 cache");
   if (q_dtype != PA_BF16 || out_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "pa_prefill_chunk takes bf16 q and out");
   if (cache->head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk supports head_dim 128");
   if (max_q_len < 0 || max_seq_len < max_q_len)
@@ -235,6 +236,8 @@ int pa_prefill_chunk(const pa_kv_cache* cache, const void* q, int32_t q_dtype, v
   pa::PrefillArgs a{};
   a.k_cache = cache->k_cache;
   a.v_cache = cache->v_cache;
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
   a.q = q;
   a.out = out;
   a.cu_q_lens = cu_q_lens;
@@ -246,7 +249,8 @@ int pa_prefill_chunk(const pa_kv_cache* cache, const void* q, int32_t q_dtype, v
   a.num_kv_heads = cache->num_kv_heads;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_q_len = max_q_len;
-  hipError_t e = pa::launch_prefill_chunk(a, cache->block_size, G, static_cast<hipStream_t>(hip_stream));
+  const int kv = cache->dtype == PA_BF16 ? pa::KV_BF16 : pa::KV_FP8;
+  hipError_t e = pa::launch_prefill_chunk(a, kv, cache->block_size, G, static_cast<hipStream_t>(hip_stream));
   if (e == hipErrorInvalidValue) return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for this shape");
   if (e != hipSuccess) return hip_fail(e, "pa_prefill_chunk launch");
   g_err[0] = 0;

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "pa_device.h"
+
 namespace pa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -23,5 +25,27 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const
 // holds key 16ks + 8h + e, which is exactly the B-operand layout of P^T for
 // the 16-key slice ks.
 __device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// Eight consecutive cache elements as the raw load (16 bytes of bf16 or 8
+// bytes of e4m3 codes) and their bf16 form, the MFMA operand.  Every e4m3
+// value is exactly a bf16 value, so the conversion is exact; the per-head
+// scale is applied outside the contraction.
+template <int KV>
+struct KvRaw {
+  using T = uint4;                                      // bf16
+  static constexpr int ES = 2;
+  __device__ static __forceinline__ uint4 to_bf16(const uint4& x) { return x; }
+};
+template <>
+struct KvRaw<KV_FP8> {
+  using T = uint2;
+  static constexpr int ES = 1;
+  __device__ static __forceinline__ uint4 to_bf16(const uint2& x) {
+    uint4 r;
+    fp8x4_to_bf16x4(x.x, r.x, r.y);
+    fp8x4_to_bf16x4(x.y, r.z, r.w);
+    return r;
+  }
+};
 
 }  // namespace pa

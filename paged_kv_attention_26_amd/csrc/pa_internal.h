@@ -53,6 +53,8 @@ constexpr int kDecodeMaxGroup = 8;
 struct PrefillArgs {
   const void* k_cache;
   const void* v_cache;
+  const float* k_scale;  // [num_kv_heads] for an fp8 cache, else unused
+  const float* v_scale;
   const void* q;
   void* out;
   const int32_t* cu_q_lens;
@@ -78,8 +80,9 @@ hipError_t launch_copy_blocks(const CopyArgs& a, int num_pairs, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int kv_kind, int head_dim, int block_size, int group,
                          int64_t upper_units, hipStream_t s);
 // bf16 cache, head_dim 128; hipErrorInvalidValue for an uncompiled combination.
-hipError_t launch_prefill_chunk(const PrefillArgs& a, int block_size, int group, hipStream_t s);
+// kv_kind: KV_BF16 or KV_FP8 (bf16 queries and output in both cases).
+hipError_t launch_prefill_chunk(const PrefillArgs& a, int kv_kind, int block_size, int group, hipStream_t s);
 // Chunks of at most 32 / group tokens; called by launch_prefill_chunk.
-hipError_t launch_verify_chunk(const PrefillArgs& a, int block_size, int group, hipStream_t s);
+hipError_t launch_verify_chunk(const PrefillArgs& a, int kv_kind, int block_size, int group, hipStream_t s);
 
 }  // namespace pa

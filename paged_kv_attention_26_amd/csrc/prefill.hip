@@ -55,7 +55,7 @@ constexpr int kPrefillSortMax = 256;
 // fewer heads) share every staged K / V tile.
 constexpr int kPrefillWaves = 8;
 
-template <int B, int G>
+template <int KV, int B, int G>
 __global__ void __launch_bounds__(kPrefillWaves * 64) prefill_kernel(PrefillArgs a, const int32_t* __restrict__ block_table,
                                                         const int32_t* __restrict__ cu_q_lens,
                                                         const int32_t* __restrict__ seq_lens) {
@@ -134,7 +134,12 @@ __global__ void __launch_bounds__(kPrefillWaves * 64) prefill_kernel(PrefillArgs
   const int32_t* table = block_table + size_t(seq) * a.max_blocks_per_seq;
   const char* kpool = static_cast<const char*>(a.k_cache);
   const char* vpool = static_cast<const char*>(a.v_cache);
-  const float c = a.scale_log2;
+  using Raw = KvRaw<KV>;
+  constexpr int ES = Raw::ES;                   // cache element bytes
+  // an fp8 code of kv head h means code * scale[h]: K's scale goes into the
+  // softmax constant, V's onto the output
+  const float c = KV == KV_FP8 ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
+  const float v_mul = KV == KV_FP8 ? a.v_scale[kvh] : 1.f;
 
   // ---- staging of one tile by the whole workgroup: each thread moves one
   // 16-byte chunk of K (row kr, column chunk kcc) and one of V^T (head dim
@@ -150,18 +155,18 @@ __global__ void __launch_bounds__(kPrefillWaves * 64) prefill_kernel(PrefillArgs
     const int b0_ = k0_ / B;                                                                                  \
     const int key_ = min(k0_ + kr, kmax);                                                                     \
     const int bk_ = key_ / B == b0_ ? (ID0) : (ID1);                                                          \
-    P##k = *reinterpret_cast<const uint4*>(kpool + ((size_t(bk_) * Hkv + kvh) * B + key_ % B) * (D * 2) +     \
-                                           kcc * 16);                                                         \
+    P##k = *reinterpret_cast<const typename Raw::T*>(kpool + ((size_t(bk_) * Hkv + kvh) * B + key_ % B) *     \
+                                                     (D * ES) + kcc * 8 * ES);                                \
     const int kb_ = min(k0_ + 8 * vkc, kmax & ~7);                                                            \
     const int bv_ = kb_ / B == b0_ ? (ID0) : (ID1);                                                           \
-    P##v = *reinterpret_cast<const uint4*>(vpool + ((size_t(bv_) * Hkv + kvh) * D + vd) * (B * 2) +           \
-                                           (kb_ % B) * 2);                                                    \
+    P##v = *reinterpret_cast<const typename Raw::T*>(vpool + ((size_t(bv_) * Hkv + kvh) * D + vd) * (B * ES) + \
+                                                     (kb_ % B) * ES);                                         \
   } while (0)
 #define PA_STAGE_STORE(P, BUF)                                                                                \
   do {                                                                                                        \
     char* sb_ = smem[BUF];                                                                                    \
-    *reinterpret_cast<uint4*>(sb_ + kr * KROW + (kcc ^ kswz(kr)) * 16) = P##k;                                \
-    *reinterpret_cast<uint4*>(sb_ + KBUF + vd * VROW + vkc * 16) = P##v;                                      \
+    *reinterpret_cast<uint4*>(sb_ + kr * KROW + (kcc ^ kswz(kr)) * 16) = Raw::to_bf16(P##k);                  \
+    *reinterpret_cast<uint4*>(sb_ + KBUF + vd * VROW + vkc * 16) = Raw::to_bf16(P##v);                        \
   } while (0)
   // block ids of a tile's (at most two) blocks, read through the scalar cache
   auto tile_ids = [&](int kt, int& id0, int& id1) __attribute__((always_inline)) {
@@ -267,7 +272,7 @@ __global__ void __launch_bounds__(kPrefillWaves * 64) prefill_kernel(PrefillArgs
   };
 
   const int last = n_tiles_wg - 1;
-  uint4 sa_k, sa_v, sb_k, sb_v;
+  typename Raw::T sa_k, sa_v, sb_k, sb_v;
   int j0, j1;
   tile_ids(0, j0, j1);
   PA_STAGE_LOAD(sa_, 0, j0, j1);
@@ -295,7 +300,7 @@ __global__ void __launch_bounds__(kPrefillWaves * 64) prefill_kernel(PrefillArgs
   // ---- normalise and store: accumulator r of d-tile dt is dim 32dt + 8(r/4) + 4hh + (r%4)
   const float l = l_run + __shfl_xor(l_run, 32);
   if (!valid_q) return;
-  const float inv = 1.f / l;
+  const float inv = v_mul / l;
   uint16_t* orow = static_cast<uint16_t*>(a.out) + (size_t(q0 + t) * Hq + head) * D + 4 * hh;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -307,10 +312,10 @@ __global__ void __launch_bounds__(kPrefillWaves * 64) prefill_kernel(PrefillArgs
     }
 }
 
-hipError_t launch_prefill_chunk(const PrefillArgs& a0, int block_size, int group, hipStream_t s) {
+hipError_t launch_prefill_chunk(const PrefillArgs& a0, int kv_kind, int block_size, int group, hipStream_t s) {
   // chunks of at most 32 / G tokens (speculative verification) fill the MFMA
   // columns with (head, token) pairs instead of 32 rows of one head
-  if (int64_t(a0.max_q_len) * group <= 32) return launch_verify_chunk(a0, block_size, group, s);
+  if (int64_t(a0.max_q_len) * group <= 32) return launch_verify_chunk(a0, kv_kind, block_size, group, s);
   PrefillArgs a = a0;
   a.num_qtiles = (a.max_q_len + 31) / 32;
   a.wg_per_pair = (group * a.num_qtiles + kPrefillWaves - 1) / kPrefillWaves;
@@ -318,14 +323,15 @@ hipError_t launch_prefill_chunk(const PrefillArgs& a0, int block_size, int group
   const int64_t wgs = ((pairs + 7) / 8) * 8 * a.wg_per_pair;
   if (wgs == 0) return hipSuccess;
   if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
-#define PA_PF(b, g) \
-  if (block_size == b && group == g) { \
-    hipLaunchKernelGGL((prefill_kernel<b, g>), dim3(uint32_t(wgs)), dim3(kPrefillWaves * 64), 0, s, a, a.block_table, \
-                       a.cu_q_lens, a.seq_lens); \
+#define PA_PF(kv, b, g) \
+  if (kv_kind == kv && block_size == b && group == g) { \
+    hipLaunchKernelGGL((prefill_kernel<kv, b, g>), dim3(uint32_t(wgs)), dim3(kPrefillWaves * 64), 0, s, a, \
+                       a.block_table, a.cu_q_lens, a.seq_lens); \
     return hipGetLastError(); \
   }
-  PA_PF(16, 1) PA_PF(16, 2) PA_PF(16, 4) PA_PF(16, 8)
-  PA_PF(32, 1) PA_PF(32, 2) PA_PF(32, 4) PA_PF(32, 8)
+#define PA_PF_G(kv, b) PA_PF(kv, b, 1) PA_PF(kv, b, 2) PA_PF(kv, b, 4) PA_PF(kv, b, 8)
+  PA_PF_G(KV_BF16, 16) PA_PF_G(KV_BF16, 32) PA_PF_G(KV_FP8, 16) PA_PF_G(KV_FP8, 32)
+#undef PA_PF_G
 #undef PA_PF
   return hipErrorInvalidValue;
 }

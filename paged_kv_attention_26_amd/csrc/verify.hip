@@ -32,7 +32,7 @@ namespace pa {
 
 constexpr int kVerifyWaves = 8;
 
-template <int B, int G>
+template <int KV, int B, int G>
 __global__ void __launch_bounds__(kVerifyWaves * 64) verify_kernel(PrefillArgs a,
                                                                   const int32_t* __restrict__ block_table,
                                                                   const int32_t* __restrict__ cu_q_lens,
@@ -66,7 +66,12 @@ __global__ void __launch_bounds__(kVerifyWaves * 64) verify_kernel(PrefillArgs a
   const int32_t* table = block_table + size_t(seq) * a.max_blocks_per_seq;
   const char* kpool = static_cast<const char*>(a.k_cache);
   const char* vpool = static_cast<const char*>(a.v_cache);
-  const float c = a.scale_log2;
+  using Raw = KvRaw<KV>;
+  constexpr int ES = Raw::ES;                   // cache element bytes
+  // an fp8 code of kv head h means code * scale[h]: K's scale goes into the
+  // softmax constant, V's onto the output
+  const float c = KV == KV_FP8 ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
+  const float v_mul = KV == KV_FP8 ? a.v_scale[kvh] : 1.f;
 
   // ---- Q^T as 8 B operands (k = 16 head dims each): row q0 + t, dims 16s + 8hh .. + 7
   uint4 qb[8];
@@ -78,7 +83,7 @@ __global__ void __launch_bounds__(kVerifyWaves * 64) verify_kernel(PrefillArgs a
   }
 
   // ---- operands of a tile (tiles past the last re-read the last one)
-  uint4 ka[8], va[4][2];
+  typename Raw::T ka[8], va[4][2];               // raw loads; converted to bf16 at their use
   const int my_key = swap23(n);                  // key of MFMA row n within a tile
   auto tile_ids = [&](int kt, int& id0, int& id1) __attribute__((always_inline)) {
     const int b0 = kt * KT / B;
@@ -89,9 +94,9 @@ __global__ void __launch_bounds__(kVerifyWaves * 64) verify_kernel(PrefillArgs a
     const int k0 = kt * KT;
     const int key = min(k0 + my_key, kmax);
     const int bid = key / B == k0 / B ? id0 : id1;
-    const char* kr = kpool + ((size_t(bid) * Hkv + kvh) * B + key % B) * (D * 2) + 16 * hh;
+    const char* kr = kpool + ((size_t(bid) * Hkv + kvh) * B + key % B) * (D * ES) + 8 * ES * hh;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) ka[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
+    for (int s = 0; s < 8; ++s) ka[s] = *reinterpret_cast<const typename Raw::T*>(kr + 16 * ES * s);
   };
   auto load_v = [&](int kt, int id0, int id1) __attribute__((always_inline)) {
     const int k0 = kt * KT;
@@ -99,9 +104,10 @@ __global__ void __launch_bounds__(kVerifyWaves * 64) verify_kernel(PrefillArgs a
     for (int ks = 0; ks < 2; ++ks) {
       const int kb = min(k0 + 16 * ks + 8 * hh, kmax & ~7);   // 8 keys of one block
       const int bid = kb / B == k0 / B ? id0 : id1;
-      const char* vb = vpool + (size_t(bid) * Hkv + kvh) * size_t(D * B * 2) + (kb % B) * 2;
+      const char* vb = vpool + (size_t(bid) * Hkv + kvh) * size_t(D * B * ES) + (kb % B) * ES;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) va[dt][ks] = *reinterpret_cast<const uint4*>(vb + size_t(32 * dt + n) * (B * 2));
+      for (int dt = 0; dt < 4; ++dt)
+        va[dt][ks] = *reinterpret_cast<const typename Raw::T*>(vb + size_t(32 * dt + n) * (B * ES));
     }
   };
 
@@ -128,7 +134,7 @@ __global__ void __launch_bounds__(kVerifyWaves * 64) verify_kernel(PrefillArgs a
     // ---- S^T = K Q^T; accumulator r = 4i + j is key k0 + swap23(8i + 4hh + j)
     f32x16_t sc = f32x16_t{};
 #pragma unroll
-    for (int st = 0; st < 8; ++st) sc = mfma32(ka[st], qb[st], sc);
+    for (int st = 0; st < 8; ++st) sc = mfma32(Raw::to_bf16(ka[st]), qb[st], sc);
     __builtin_amdgcn_sched_barrier(0);
     load_k(nxt, id0, id1);                                  // next tile's keys fly during softmax + PV
     __builtin_amdgcn_sched_barrier(0);
@@ -169,6 +175,11 @@ __global__ void __launch_bounds__(kVerifyWaves * 64) verify_kernel(PrefillArgs a
     for (int ks = 0; ks < 2; ++ks)
       pb[ks] = make_uint4(pack_bf16x2(p[8 * ks + 0], p[8 * ks + 1]), pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]),
                           pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]), pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7]));
+    uint4 vb16[4][2];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) vb16[dt][ks] = Raw::to_bf16(va[dt][ks]);
     if (k0 + KT > key_end) {                                // zero V rows of keys past the end (NaN poison)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -179,14 +190,14 @@ __global__ void __launch_bounds__(kVerifyWaves * 64) verify_kernel(PrefillArgs a
           msk[e] = (kb + 2 * e < key_end ? 0x0000FFFFu : 0u) | (kb + 2 * e + 1 < key_end ? 0xFFFF0000u : 0u);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          va[dt][ks].x &= msk[0]; va[dt][ks].y &= msk[1]; va[dt][ks].z &= msk[2]; va[dt][ks].w &= msk[3];
+          vb16[dt][ks].x &= msk[0]; vb16[dt][ks].y &= msk[1]; vb16[dt][ks].z &= msk[2]; vb16[dt][ks].w &= msk[3];
         }
       }
     }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      o[dt] = mfma32(va[dt][0], pb[0], o[dt]);
-      o[dt] = mfma32(va[dt][1], pb[1], o[dt]);
+      o[dt] = mfma32(vb16[dt][0], pb[0], o[dt]);
+      o[dt] = mfma32(vb16[dt][1], pb[1], o[dt]);
     }
     __builtin_amdgcn_sched_barrier(0);
     load_v(nxt, id0, id1);                                  // its values fly during its S^T
@@ -230,24 +241,25 @@ __global__ void __launch_bounds__(kVerifyWaves * 64) verify_kernel(PrefillArgs a
     acc[4] = fmaf(wt, x1.x, acc[4]); acc[5] = fmaf(wt, x1.y, acc[5]);
     acc[6] = fmaf(wt, x1.z, acc[6]); acc[7] = fmaf(wt, x1.w, acc[7]);
   }
-  const float inv = 1.f / L;
+  const float inv = v_mul / L;
   uint16_t* orow = static_cast<uint16_t*>(a.out) + (size_t(q0 + ct) * Hq + kvh * G + cg) * D + d0;
   *reinterpret_cast<uint4*>(orow) = make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
                                                pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
 }
 
-hipError_t launch_verify_chunk(const PrefillArgs& a, int block_size, int group, hipStream_t s) {
+hipError_t launch_verify_chunk(const PrefillArgs& a, int kv_kind, int block_size, int group, hipStream_t s) {
   const int64_t wgs = int64_t(a.num_seqs) * a.num_kv_heads;
   if (wgs == 0) return hipSuccess;
   if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
-#define PA_VF(b, g) \
-  if (block_size == b && group == g) { \
-    hipLaunchKernelGGL((verify_kernel<b, g>), dim3(uint32_t(wgs)), dim3(kVerifyWaves * 64), 0, s, a, a.block_table, \
-                       a.cu_q_lens, a.seq_lens); \
+#define PA_VF(kv, b, g) \
+  if (kv_kind == kv && block_size == b && group == g) { \
+    hipLaunchKernelGGL((verify_kernel<kv, b, g>), dim3(uint32_t(wgs)), dim3(kVerifyWaves * 64), 0, s, a, \
+                       a.block_table, a.cu_q_lens, a.seq_lens); \
     return hipGetLastError(); \
   }
-  PA_VF(16, 1) PA_VF(16, 2) PA_VF(16, 4) PA_VF(16, 8)
-  PA_VF(32, 1) PA_VF(32, 2) PA_VF(32, 4) PA_VF(32, 8)
+#define PA_VF_G(kv, b) PA_VF(kv, b, 1) PA_VF(kv, b, 2) PA_VF(kv, b, 4) PA_VF(kv, b, 8)
+  PA_VF_G(KV_BF16, 16) PA_VF_G(KV_BF16, 32) PA_VF_G(KV_FP8, 16) PA_VF_G(KV_FP8, 32)
+#undef PA_VF_G
 #undef PA_VF
   return hipErrorInvalidValue;
 }

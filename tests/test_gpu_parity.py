@@ -227,10 +227,10 @@ def test_fp8_codes_round_trip_through_store_and_decode():
 
 
 # ------------------------------------------------------------ chunked prefill
-def chunk_batch(name, P, q, B=16, Hq=32, Hkv=8, seed=41):
+def chunk_batch(name, P, q, B=16, Hq=32, Hkv=8, seed=41, kv="bf16"):
     rng = np.random.default_rng(seed)
     n = len(P)
-    return W.paged_batch(name, seed, kv_dtype="bf16", io_dtype="bf16", Hq=Hq, Hkv=Hkv, d=128, B=B,
+    return W.paged_batch(name, seed, kv_dtype=kv, io_dtype="bf16", Hq=Hq, Hkv=Hkv, d=128, B=B,
                          prior_lens=P, new_lens=q, is_chunk=np.ones(n, bool), rng=rng)
 
 
@@ -250,6 +250,11 @@ CHUNKS = {
     "verify-g2": lambda: chunk_batch("verify-g2", [40, 1000], [16, 9], Hq=16, Hkv=8),
     "verify-g8": lambda: chunk_batch("verify-g8", [40, 1000, 0], [4, 3, 4], Hq=32, Hkv=4),
     "verify-batch-small": lambda: W.verify_batch(small=True),
+    # fp8 e4m3 caches (bf16 queries): both kernels
+    "fp8-c4s": lambda: W.config4(small=True, kv_dtype="fp8"),
+    "fp8-ragged-b32": lambda: chunk_batch("fp8-ragged-b32", [5, 100, 33, 512, 0], [1, 31, 33, 97, 129], B=32,
+                                          kv="fp8"),
+    "fp8-verify": lambda: chunk_batch("fp8-verify", [0, 15, 1023, 4100], [5, 8, 1, 5], kv="fp8"),
 }
 
 
@@ -268,12 +273,12 @@ def test_prefill_chunk_matches_oracle(name):
     assert np.all(np.isfinite(got))
     err = np.max(np.abs(got - ref))
     say(f"      max abs err {err:.3e}")
-    assert err < TOL["bf16"]
+    assert err < TOL[batch.kv_dtype]
     if (~batch.is_chunk).any():                      # the mixed batch's decode half too
         dref = OS.decode_ref(batch, st)
         derr = np.max(np.abs(out_f64(runner.decode_step(g)) - dref))
         say(f"      decode max abs err {derr:.3e}")
-        assert derr < TOL["bf16"]
+        assert derr < TOL[batch.kv_dtype]
 
 
 def test_prefill_chunk_of_one_row_matches_decode():

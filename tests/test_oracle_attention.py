@@ -115,6 +115,14 @@ def test_verify_chunk_matches_dense_sdpa():
     assert np.max(np.abs(OS.chunk_ref(batch, st) - dense_chunk(batch))) < 1e-12
 
 
+def test_fp8_chunk_matches_dense_sdpa():
+    """Chunks over an fp8 cache: the stored codes times the per-head scales,
+    attended densely with the end-aligned causal mask."""
+    batch = W.config4(small=True, kv_dtype="fp8")
+    st = OS.build(batch)
+    assert np.max(np.abs(OS.chunk_ref(batch, st) - dense_chunk(batch))) < 1e-12
+
+
 def test_fp8_decode_matches_dense_sdpa():
     """Shared-prefix beams of the small fork config as a plain decode batch."""
     fb = W.config5(small=True)

@@ -217,8 +217,9 @@ def config3_at_block(base: PagedBatch, block_size: int) -> PagedBatch:
     return b
 
 
-def config4(small=False) -> PagedBatch:
-    """Mixed chunked-prefill batch: 8 chunks of 512 on prefixes U{0..7680} + 64 decodes U{256..4096}."""
+def config4(small=False, kv_dtype="bf16") -> PagedBatch:
+    """Mixed chunked-prefill batch: 8 chunks of 512 on prefixes U{0..7680} + 64 decodes U{256..4096}.
+    kv_dtype "fp8" stores the same values as e4m3 with per-head scales."""
     seed = 4 if not small else 104
     rng = np.random.default_rng(seed)
     if small:
@@ -232,8 +233,9 @@ def config4(small=False) -> PagedBatch:
     prior = np.concatenate([P, Ld - 1])
     new = np.concatenate([np.full(n_chunk, chunk), np.ones(n_dec, np.int64)])
     is_chunk = np.concatenate([np.ones(n_chunk, bool), np.zeros(n_dec, bool)])
-    return paged_batch("mixed-chunked-prefill" if not small else "mixed-chunked-prefill-small", seed,
-                       kv_dtype="bf16", io_dtype="bf16", Hq=32, Hkv=8, d=128, B=16,
+    name = "mixed-chunked-prefill" if not small else "mixed-chunked-prefill-small"
+    return paged_batch(name if kv_dtype == "bf16" else name + "-" + kv_dtype, seed,
+                       kv_dtype=kv_dtype, io_dtype="bf16", Hq=32, Hkv=8, d=128, B=16,
                        prior_lens=prior, new_lens=new, is_chunk=is_chunk, rng=rng)
 
 
