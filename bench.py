@@ -15,6 +15,7 @@ measurements, and the oracle's CPU throughput on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import copy
 import json
 import math
 import os
@@ -86,7 +87,7 @@ def timed_calls(fn, reps, warm=3):
     return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
 
 
-EXTRA_GROUPS = ("long_context", "mixed", "fork", "verify")
+EXTRA_GROUPS = ("long_context", "mixed", "fork", "verify", "handoff")
 
 
 def extras(pa, runner, W, torch, groups=EXTRA_GROUPS):
@@ -140,6 +141,28 @@ def extras(pa, runner, W, torch, groups=EXTRA_GROUPS):
                                 TFLOPs=round(fl / med / 1e9, 1), ms=round(med, 4), p10_ms=round(p10, 4),
                                 p90_ms=round(p90, 4), kv_bytes=byt, tokens=int(np.sum(tl)))
         del g
+    if "handoff" in groups:
+        # prefill -> decode KV hand-off of the Qwen3-8B layer's 32 sequences:
+        # pack out of the paged pools, store into another cache's own blocks
+        b = W.config2()
+        g = runner.prepare(b)
+        runner.store_step(g)
+        rows = int(np.sum(b.total_lens))
+        k = torch.empty((rows, b.num_kv_heads, b.head_dim), dtype=torch.bfloat16, device="cuda")
+        v = torch.empty_like(k)
+        med_p, _, _ = timed_calls(lambda: runner.pack_all(g, k_out=k, v_out=v), 20)
+        d = copy.copy(b)
+        d.free_order = np.random.default_rng(2002).permutation(b.num_blocks)
+        gd = runner.prepare(d, fill=False)
+        slots = runner.all_slots(gd)
+        med_u, _, _ = timed_calls(lambda: pa.store_kv(gd.cache, k, v, slots), 20)
+        byt = kv_bytes(b.total_lens, b.num_kv_heads, b.head_dim, 2)
+        out["handoff_pack"] = dict(GBps=round(2 * byt / med_p / 1e6, 1), frac=round(2 * byt / med_p / 1e6 / HBM_PEAK_GBS, 4),
+                                   ms=round(med_p, 4), kv_bytes=byt)
+        out["handoff_unpack_store"] = dict(GBps=round((2 * byt + 4 * rows) / med_u / 1e6, 1),
+                                           frac=round((2 * byt + 4 * rows) / med_u / 1e6 / HBM_PEAK_GBS, 4),
+                                           ms=round(med_u, 4))
+        del g, gd
     if "fork" in groups:
         fb = W.config5()
         gf = runner.run_fork(fb)

@@ -92,7 +92,8 @@ typedef struct {
  *   k_cache[slot / bs][h][slot % bs][:] = enc(k_new[t][h][:])
  *   v_cache[slot / bs][h][:][slot % bs] = enc(v_new[t][h][:])
  * enc is the identity when in_dtype == cache dtype (F32->F32, BF16->BF16,
- * bit-exact).  For an FP8 cache in_dtype must be BF16 and
+ * FP8_E4M3->FP8_E4M3: codes as they are, e.g. rows from pa_pack_kv;
+ * bit-exact).  Into an FP8 cache, BF16 input is quantised:
  * enc(x) = e4m3fn_round_nearest_even_saturate(float(x) / scale[h]) with an
  * IEEE fp32 division; magnitudes above 448 saturate to +-448, NaN stays NaN.
  * Two tokens with the same slot in one call: which one lands is unspecified.
@@ -110,6 +111,24 @@ int pa_store_kv(const pa_kv_cache* cache, const void* k_new, const void* v_new, 
  * call (then the copy order cannot matter).  num_pairs == 0 is a no-op. */
 int pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src_dst, int32_t num_pairs,
                    void* hip_stream);
+
+/* Gather sequences' cached K/V out of the paged pools into contiguous token
+ * rows: the prefill side's half of the KV hand-off to a decode instance
+ * (nanoPD page, 异步KV传输; PD-engineering page section 3).  The receiving
+ * side stores the rows with pa_store_kv and its own slot_mapping (for an
+ * fp8 cache with in_dtype FP8_E4M3, codes unchanged).
+ *   block_table : [num_seqs][max_blocks_per_seq] int32, as for pa_decode
+ *   seq_lens    : [num_seqs] int32, tokens of each sequence (0 allowed)
+ *   cu_rows     : [num_seqs] int32, first output row of each sequence
+ *   k_out, v_out: [rows][num_kv_heads][head_dim] of the cache dtype
+ * For every sequence s, token i < seq_lens[s] and kv head h (bit-exact):
+ *   k_out[cu_rows[s] + i][h][:] = k_cache[table[s][i / bs]][h][i % bs][:]
+ *   v_out[cu_rows[s] + i][h][:] = v_cache[table[s][i / bs]][h][:][i % bs]
+ * max_seq_len is a host upper bound of seq_lens (sizes the launch; at most
+ * 65535 blocks).  Rows of different sequences must not overlap. */
+int pa_pack_kv(const pa_kv_cache* cache, const int32_t* block_table, int32_t max_blocks_per_seq,
+               const int32_t* seq_lens, const int32_t* cu_rows, int32_t num_seqs, int32_t max_seq_len,
+               void* k_out, void* v_out, void* hip_stream);
 
 /* Bytes of device workspace pa_decode needs (host call, no HIP): two partial
  * results per wavefront for at most 4096 wavefronts and 8 query heads per kv

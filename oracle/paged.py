@@ -111,6 +111,26 @@ def copy_blocks(k_cache, v_cache, pairs):
         v_cache[dst] = v_cache[src]
 
 
+def pack_kv(k_cache, v_cache, block_tables, seq_lens):
+    """The KV hand-off gather (nanoPD page, 异步KV传输; PD-engineering page
+    section 3): every sequence's stored K and V, token by token, as rows
+    [sum(seq_lens), Hkv, d] of the cache's own storage (no decoding), in
+    sequence order.  Row i of sequence s is its token i, read at
+    ``cache[table[s][i // B], h, i % B, :]`` (K) and ``[.., h, :, i % B]`` (V).
+    """
+    B = k_cache.shape[2]
+    ks, vs = [], []
+    for table_row, n in zip(block_tables, seq_lens):
+        i = np.arange(int(n))
+        blk = np.asarray(table_row, dtype=np.int64)[i // B]
+        off = i % B
+        ks.append(k_cache[blk, :, off, :])
+        vs.append(v_cache[blk, :, :, off])
+    shape = (0,) + k_cache.shape[1:2] + k_cache.shape[3:]
+    return (np.concatenate(ks) if ks else np.zeros(shape, k_cache.dtype),
+            np.concatenate(vs) if vs else np.zeros(shape, v_cache.dtype))
+
+
 # --------------------------------------------------------------- attention
 def gather_kv(k_cache, v_cache, kv_dtype, table_row, n_tokens, k_scale=None, v_scale=None):
     """Logical tokens 0..n-1 of one sequence, read through its block table.

@@ -87,11 +87,37 @@ def store_kv(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, slot_mapp
     shape = (T, cache.num_kv_heads, cache.head_dim)
     if tuple(k_new.shape) != shape or tuple(v_new.shape) != shape:
         raise ValueError(f"k_new / v_new must be {shape}")
-    io = DTYPE_CODES["f32"] if cache.dtype == "f32" else DTYPE_CODES["bf16"]
-    L.check(L.lib().pa_store_kv(C.byref(cache.desc), _dev(k_new, "k_new", cache.io_dtype),
-                                _dev(v_new, "v_new", cache.io_dtype), io,
+    if cache.dtype == "fp8" and k_new.dtype == CACHE_TORCH["fp8"]:   # e4m3 codes, stored as they are
+        io, tdt = DTYPE_CODES["fp8"], CACHE_TORCH["fp8"]
+    else:
+        io, tdt = (DTYPE_CODES["f32"] if cache.dtype == "f32" else DTYPE_CODES["bf16"]), cache.io_dtype
+    L.check(L.lib().pa_store_kv(C.byref(cache.desc), _dev(k_new, "k_new", tdt), _dev(v_new, "v_new", tdt), io,
                                 _dev(slot_mapping, "slot_mapping", torch.int32), T, _stream(stream)),
             "pa_store_kv")
+
+
+def pack_kv(cache: KVCache, block_table: torch.Tensor, seq_lens: torch.Tensor, cu_rows: torch.Tensor,
+            max_seq_len: int, rows: int, k_out: Optional[torch.Tensor] = None,
+            v_out: Optional[torch.Tensor] = None, stream=None):
+    """Gather the sequences' cached K/V into contiguous rows [rows, Hkv, D] of
+    the cache dtype (pa_pack_kv).  Returns (k_out, v_out)."""
+    S = seq_lens.numel()
+    if block_table.dim() != 2 or block_table.shape[0] != S or cu_rows.numel() != S:
+        raise ValueError("block_table must be [S, max_blocks], seq_lens and cu_rows [S]")
+    shape = (rows, cache.num_kv_heads, cache.head_dim)
+    tdt = CACHE_TORCH[cache.dtype]
+    if k_out is None:
+        k_out = torch.empty(shape, dtype=tdt, device=cache.k_cache.device)
+    if v_out is None:
+        v_out = torch.empty(shape, dtype=tdt, device=cache.k_cache.device)
+    if tuple(k_out.shape) != shape or tuple(v_out.shape) != shape:
+        raise ValueError(f"k_out / v_out must be {shape}")
+    L.check(L.lib().pa_pack_kv(C.byref(cache.desc), _dev(block_table, "block_table", torch.int32),
+                               block_table.shape[1], _dev(seq_lens, "seq_lens", torch.int32),
+                               _dev(cu_rows, "cu_rows", torch.int32), S, int(max_seq_len),
+                               _dev(k_out, "k_out", tdt), _dev(v_out, "v_out", tdt), _stream(stream)),
+            "pa_pack_kv")
+    return k_out, v_out
 
 
 def copy_blocks(cache: KVCache, pairs: torch.Tensor, stream=None) -> None:

@@ -112,13 +112,17 @@ int pa_store_kv(const pa_kv_cache* cache, const void* k_new, const void* v_new, 
   if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens %d < 0", num_tokens);
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping) return fail(PA_ERR_NULL, "k_new / v_new / slot_mapping is NULL");
-  if (in_dtype != io_dtype_for(cache->dtype))
+  const bool raw_fp8 = cache->dtype == PA_FP8_E4M3 && in_dtype == PA_FP8_E4M3;   // codes as they are
+  if (in_dtype != io_dtype_for(cache->dtype) && !raw_fp8)
     return fail(PA_ERR_DTYPE, "store into a %s cache takes %s input",
                 cache->dtype == PA_F32 ? "f32" : cache->dtype == PA_BF16 ? "bf16" : "fp8",
-                cache->dtype == PA_F32 ? "f32" : "bf16");
+                cache->dtype == PA_F32 ? "f32" : cache->dtype == PA_BF16 ? "bf16" : "bf16 or fp8");
   pa::StoreArgs a{cache->k_cache, cache->v_cache, cache->k_scale, cache->v_scale, k_new, v_new, slot_mapping,
                   num_tokens, cache->num_kv_heads, cache->block_size, cache->head_dim};
-  const int kv = cache->dtype == PA_F32 ? pa::KV_F32 : cache->dtype == PA_BF16 ? pa::KV_BF16 : pa::KV_FP8;
+  const int kv = cache->dtype == PA_F32    ? pa::KV_F32
+                 : cache->dtype == PA_BF16 ? pa::KV_BF16
+                 : raw_fp8                 ? pa::KV_FP8_RAW
+                                           : pa::KV_FP8;
   hipError_t e = pa::launch_store_kv(a, kv, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "pa_store_kv launch");
   g_err[0] = 0;
@@ -135,6 +139,30 @@ int pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src_dst, int32_t num
                  size_t(cache->num_kv_heads) * cache->block_size * cache->head_dim * elem_bytes(cache->dtype)};
   hipError_t e = pa::launch_copy_blocks(a, num_pairs, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "pa_copy_blocks launch");
+  g_err[0] = 0;
+  return PA_OK;
+}
+
+int pa_pack_kv(const pa_kv_cache* cache, const int32_t* block_table, int32_t max_blocks_per_seq,
+               const int32_t* seq_lens, const int32_t* cu_rows, int32_t num_seqs, int32_t max_seq_len, void* k_out,
+               void* v_out, void* hip_stream) {
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  if (num_seqs < 0 || num_seqs > kMaxSeqs) return fail(PA_ERR_SHAPE, "num_seqs %d outside 0..%d", num_seqs, kMaxSeqs);
+  if (max_seq_len < 0) return fail(PA_ERR_SHAPE, "max_seq_len %d < 0", max_seq_len);
+  const int64_t blocks = (int64_t(max_seq_len) + cache->block_size - 1) / cache->block_size;
+  if (max_blocks_per_seq < blocks || max_blocks_per_seq <= 0)
+    return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d < %lld blocks of max_seq_len", max_blocks_per_seq,
+                (long long)blocks);
+  if (blocks > 65535) return fail(PA_ERR_UNSUPPORTED, "max_seq_len %d: more than 65535 blocks", max_seq_len);
+  if (num_seqs == 0 || max_seq_len == 0) return PA_OK;
+  if (!block_table || !seq_lens || !cu_rows || !k_out || !v_out)
+    return fail(PA_ERR_NULL, "block_table / seq_lens / cu_rows / k_out / v_out is NULL");
+  pa::PackArgs a{cache->k_cache, cache->v_cache, block_table, seq_lens, cu_rows, k_out, v_out,
+                 cache->num_kv_heads, cache->block_size, cache->head_dim, max_blocks_per_seq};
+  hipError_t e = pa::launch_pack_kv(a, int(elem_bytes(cache->dtype)), num_seqs, int(blocks),
+                                    static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_pack_kv launch");
   g_err[0] = 0;
   return PA_OK;
 }

@@ -9,7 +9,8 @@
 namespace pa {
 
 // Cache element kinds the kernels are compiled for.
-enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+// KV_FP8 stores bf16 input as e4m3 codes; KV_FP8_RAW stores e4m3 codes as they are.
+enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_FP8_RAW = 3 };
 
 struct StoreArgs {
   void* k_cache;
@@ -27,6 +28,17 @@ struct CopyArgs {
   void* v_cache;
   const int32_t* pairs;
   size_t block_bytes;  // bytes of one block in one pool
+};
+
+struct PackArgs {
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* cu_rows;
+  void* k_out;
+  void* v_out;
+  int32_t num_kv_heads, block_size, head_dim, max_blocks_per_seq;
 };
 
 struct DecodeArgs {
@@ -76,6 +88,8 @@ DecodeWorkspace decode_workspace_layout(int64_t head_dim);
 
 hipError_t launch_store_kv(const StoreArgs& a, int kv_kind, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyArgs& a, int num_pairs, hipStream_t s);
+// elem_bytes 1, 2 or 4; grid num_seqs x max_blocks_used.
+hipError_t launch_pack_kv(const PackArgs& a, int elem_bytes, int num_seqs, int max_blocks_used, hipStream_t s);
 // Returns hipErrorInvalidValue for a combination without a compiled kernel.
 hipError_t launch_decode(const DecodeArgs& a, int kv_kind, int head_dim, int block_size, int group,
                          int64_t upper_units, hipStream_t s);

@@ -5,6 +5,9 @@
 // kernel; the serving-stack page, section 2.3, places a sequence's new token
 // at offset length % block_size of its last block.  Here a slot is
 // physical_block * block_size + offset.
+// Pack: the inverse gather, a request's cached K/V out of its blocks into
+// contiguous token rows, the form in which the prefill side hands KV to the
+// decode side (nanoPD page, 异步KV传输; PD-engineering page section 3).
 // Copy: copy on write of a shared block before a forked sequence writes into
 // it (nanoPD page, paged KV cache with CoW; serving-stack page 2.3, cow()).
 #include "pa_device.h"
@@ -19,7 +22,7 @@ namespace pa {
 //     block write neighbouring elements of each transposed head-dim row.
 template <int KV>
 __global__ void __launch_bounds__(256) store_kv_kernel(StoreArgs a) {
-  constexpr int IN_ES = (KV == KV_F32) ? 4 : 2;            // input element bytes
+  constexpr int IN_ES = (KV == KV_F32) ? 4 : (KV == KV_FP8_RAW ? 1 : 2);   // input element bytes
   constexpr int OUT_ES = (KV == KV_F32) ? 4 : (KV == KV_BF16 ? 2 : 1);
   constexpr int EPC = 16 / IN_ES;                          // elements per 16-byte chunk
   const int h = blockIdx.y;
@@ -86,6 +89,9 @@ __global__ void __launch_bounds__(256) store_kv_kernel(StoreArgs a) {
         *reinterpret_cast<uint16_t*>(vrow + size_t(d0 + 2 * e) * BS * 2) = uint16_t(w[e] & 0xFFFFu);
         *reinterpret_cast<uint16_t*>(vrow + size_t(d0 + 2 * e + 1) * BS * 2) = uint16_t(w[e] >> 16);
       }
+    } else if constexpr (KV == KV_FP8_RAW) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) *reinterpret_cast<uint8_t*>(vrow + size_t(d0 + e) * BS) = uint8_t(w[e >> 2] >> (8 * (e & 3)));
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -111,12 +117,90 @@ __global__ void __launch_bounds__(256) copy_blocks_kernel(CopyArgs a) {
   }
 }
 
+// One workgroup = one (block, kv head) tile of one sequence.  K rows leave as
+// they are (16-byte chunks, contiguous on both sides); the transposed V tile
+// goes through LDS and leaves as token rows.
+template <int ES>
+__global__ void __launch_bounds__(256) pack_kv_kernel(PackArgs a) {
+  constexpr int EPC = 16 / ES;                             // elements per 16-byte chunk
+  __shared__ __attribute__((aligned(16))) char s_v[32 * 128 * ES];   // [token][dim], at most B 32 x d 128
+  const int seq = blockIdx.x, bi = blockIdx.y, h = blockIdx.z;
+  const int H = a.num_kv_heads, D = a.head_dim, BS = a.block_size;
+  const int L = a.seq_lens[seq];
+  if (bi * BS >= L) return;                                // whole workgroup
+  const int ntok = min(BS, L - bi * BS);
+  const int blk = a.block_table[size_t(seq) * a.max_blocks_per_seq + bi];
+  const size_t row0 = size_t(a.cu_rows[seq]) + size_t(bi) * BS;
+  const int cpr = D / EPC;                                 // 16-byte chunks per token row
+  const int cpv = BS / EPC;                                // 16-byte chunks per transposed V row
+  const char* kc = static_cast<const char*>(a.k_cache);
+  const char* vc = static_cast<const char*>(a.v_cache);
+  char* ko = static_cast<char*>(a.k_out);
+  char* vo = static_cast<char*>(a.v_out);
+  // every load of the thread goes out before its first store
+  const char* ktile = kc + (size_t(blk) * H + h) * size_t(BS) * D * ES;
+  const char* vtile = vc + (size_t(blk) * H + h) * size_t(D) * BS * ES;
+  const int nk = ntok * cpr, nv = D * cpv;
+  // (loads are unconditional, clamped to the last chunk, so that they stay
+  // in registers and all fly together; only the stores are guarded)
+  constexpr int NI = (ES == 1) ? 1 : (ES == 2 ? 2 : 4);   // chunks per thread at most (block 32, d 128)
+  uint4 kx[NI], vx[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int c = min(int(threadIdx.x) + 256 * i, nk - 1);
+    kx[i] = *reinterpret_cast<const uint4*>(ktile + (size_t(c / cpr) * D) * ES + (c % cpr) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int c = min(int(threadIdx.x) + 256 * i, nv - 1);
+    vx[i] = *reinterpret_cast<const uint4*>(vtile + (size_t(c / cpv) * BS + (c % cpv) * EPC) * ES);
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < nk)
+      *reinterpret_cast<uint4*>(ko + ((row0 + c / cpr) * H + h) * size_t(D) * ES + (c % cpr) * 16) = kx[i];
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {                           // transpose [dim][token] -> [token][dim]
+    const int c = threadIdx.x + 256 * i;
+    if (c >= nv) continue;
+    const int dim = c / cpv, t0 = (c % cpv) * EPC;
+    const uint32_t w[4] = {vx[i].x, vx[i].y, vx[i].z, vx[i].w};
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      char* dst = s_v + (size_t(t0 + e) * D + dim) * ES;
+      if constexpr (ES == 4) *reinterpret_cast<uint32_t*>(dst) = w[e];
+      else if constexpr (ES == 2) *reinterpret_cast<uint16_t*>(dst) = uint16_t(w[e >> 1] >> (16 * (e & 1)));
+      else *reinterpret_cast<uint8_t*>(dst) = uint8_t(w[e >> 2] >> (8 * (e & 3)));
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < nk; c += 256) {
+    const int tok = c / cpr, cc = c % cpr;
+    *reinterpret_cast<uint4*>(vo + ((row0 + tok) * H + h) * size_t(D) * ES + cc * 16) =
+        *reinterpret_cast<const uint4*>(s_v + (size_t(tok) * D) * ES + cc * 16);
+  }
+}
+
+hipError_t launch_pack_kv(const PackArgs& a, int es, int num_seqs, int max_blocks_used, hipStream_t s) {
+  if (num_seqs == 0 || max_blocks_used == 0) return hipSuccess;
+  dim3 grid(num_seqs, max_blocks_used, a.num_kv_heads);
+  switch (es) {
+    case 4: hipLaunchKernelGGL(pack_kv_kernel<4>, grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(pack_kv_kernel<2>, grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL(pack_kv_kernel<1>, grid, dim3(256), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_store_kv(const StoreArgs& a, int kv, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
   dim3 grid((a.num_tokens + 63) / 64, a.num_kv_heads);
   switch (kv) {
     case KV_F32: hipLaunchKernelGGL(store_kv_kernel<KV_F32>, grid, dim3(256), 0, s, a); break;
     case KV_BF16: hipLaunchKernelGGL(store_kv_kernel<KV_BF16>, grid, dim3(256), 0, s, a); break;
+    case KV_FP8_RAW: hipLaunchKernelGGL(store_kv_kernel<KV_FP8_RAW>, grid, dim3(256), 0, s, a); break;
     default: hipLaunchKernelGGL(store_kv_kernel<KV_FP8>, grid, dim3(256), 0, s, a); break;
   }
   return hipGetLastError();

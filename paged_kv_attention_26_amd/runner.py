@@ -114,6 +114,28 @@ def decode_step(g: GpuBatch, out=None, partition_tokens=0, workspace=None) -> to
                      partition_tokens=partition_tokens, workspace=workspace)
 
 
+def pack_all(g: GpuBatch, device="cuda", k_out=None, v_out=None):
+    """pa_pack_kv of every sequence's tokens (cached and stepped), in order."""
+    lens = np.asarray(g.batch.total_lens, dtype=np.int64)
+    cu = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
+    table = _t(_table_rows(g.tables, g.pad), device)
+    return pa.pack_kv(g.cache, table, _t(lens.astype(np.int32), device), _t(cu, device), int(lens.max(initial=0)),
+                      int(lens.sum()), k_out=k_out, v_out=v_out)
+
+
+def all_slots(g: GpuBatch, device="cuda") -> torch.Tensor:
+    """The slots of every sequence's tokens (cached, then stepped), in
+    sequence order: where packed rows of the same batch land in g's cache."""
+    pri, stp = g.prior_slots.cpu().numpy(), g.step_slots.cpu().numpy()
+    out, pi, si = [], 0, 0
+    for i in range(g.batch.num_seqs):
+        p, n = int(g.batch.prior_lens[i]), int(g.batch.new_lens[i])
+        out.append(np.concatenate([pri[pi:pi + p], stp[si:si + n]]))
+        pi += p
+        si += n
+    return _t(np.concatenate(out).astype(np.int32), device)
+
+
 def chunk_step(g: GpuBatch, out=None) -> torch.Tensor:
     c = g.chunk
     return pa.prefill_chunk(g.cache, c["q"], c["cu"], c["seq_lens"], c["table"], c["max_q"], c["max_seq"],

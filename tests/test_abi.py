@@ -95,10 +95,32 @@ def test_store_and_copy_reject_bad_arguments():
     assert lib.pa_store_kv(C.byref(c), FAKE, FAKE, L.PA_BF16, FAKE, -1, None) == L.PA_ERR_SHAPE
     assert lib.pa_store_kv(C.byref(c), FAKE, FAKE, L.PA_BF16, FAKE, 0, None) == L.PA_OK
     f8 = cache(dtype=L.PA_FP8_E4M3, k_scale=FAKE, v_scale=FAKE)
-    assert lib.pa_store_kv(C.byref(f8), FAKE, FAKE, L.PA_FP8_E4M3, FAKE, 4, None) == L.PA_ERR_DTYPE
+    assert lib.pa_store_kv(C.byref(f8), FAKE, FAKE, L.PA_F32, FAKE, 4, None) == L.PA_ERR_DTYPE
+    assert lib.pa_store_kv(C.byref(c), FAKE, FAKE, L.PA_FP8_E4M3, FAKE, 4, None) == L.PA_ERR_DTYPE
     assert lib.pa_copy_blocks(C.byref(c), None, 3, None) == L.PA_ERR_NULL
     assert lib.pa_copy_blocks(C.byref(c), FAKE, -2, None) == L.PA_ERR_SHAPE
     assert lib.pa_copy_blocks(C.byref(c), FAKE, 0, None) == L.PA_OK
+
+
+def test_pack_rejects_bad_arguments():
+    lib = L.lib()
+    c = cache()                                        # block 16
+    ok = dict(table=FAKE, width=4, lens=FAKE, cu=FAKE, S=2, max_len=64, k=FAKE, v=FAKE)
+
+    def call(cc, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.pa_pack_kv(C.byref(cc) if cc is not None else None, a["table"], a["width"], a["lens"], a["cu"],
+                              a["S"], a["max_len"], a["k"], a["v"], None)
+    assert call(None) == L.PA_ERR_NULL
+    assert call(c, S=-1) == L.PA_ERR_SHAPE
+    assert call(c, max_len=-5) == L.PA_ERR_SHAPE
+    assert call(c, width=3) == L.PA_ERR_SHAPE        # 64 tokens need 4 blocks
+    assert call(c, k=None) == L.PA_ERR_NULL
+    assert call(c, cu=None) == L.PA_ERR_NULL
+    assert call(c, S=0) == L.PA_OK                   # nothing to do, nothing launched
+    assert call(c, max_len=0) == L.PA_OK
+    assert call(cache(dtype=9)) == L.PA_ERR_DTYPE
 
 
 def test_prefill_rejects_bad_arguments():

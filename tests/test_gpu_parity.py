@@ -6,6 +6,7 @@ must keep their NaN poison); attention within max-abs 1e-4 (fp32 cache),
 allocation decisions (the native block manager equals the oracle's, checked
 on the CPU), and every input comes from the seeded generators.
 """
+import copy
 import sys
 
 import numpy as np
@@ -314,6 +315,51 @@ def test_prefill_full_mixed_batch_sampled():
         err = np.max(np.abs(out[cu[j]:cu[j + 1]] - ref))
         say(f"      seq {j} (prefix {int(batch.prior_lens[i])}) max abs err {err:.3e}")
         assert err < TOL["bf16"]
+
+
+# ------------------------------------------------ pack (KV hand-off)
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s32", "edge16", "skew"])
+def test_pack_is_bit_exact(name):
+    from oracle import paged
+    from paged_kv_attention_26_amd import runner
+    say(f"[gpu] pack {name}")
+    batch = SMALL[name]()
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    k, v = runner.pack_all(g)
+    torch.cuda.synchronize()
+    st = OS.build(batch)
+    wk, wv = paged.pack_kv(st.kc, st.vc, st.tables, batch.total_lens)
+    assert np.array_equal(bits(k, batch.kv_dtype), oracle_bits(wk, batch.kv_dtype))
+    assert np.array_equal(bits(v, batch.kv_dtype), oracle_bits(wv, batch.kv_dtype))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_handoff_round_trip(kv):
+    """Pack every sequence out of one cache and store the rows into another
+    cache with its own block layout (fp8: codes stored as they are): the
+    second cache packs to the same bytes and decodes bit-identically."""
+    from paged_kv_attention_26_amd import binding as pa, runner
+    say(f"[gpu] hand-off round trip {kv}")
+    src = W.config2(small=True)
+    if kv == "fp8":
+        src = W.paged_batch("handoff-fp8", 12, kv_dtype="fp8", io_dtype="bf16", Hq=32, Hkv=8, d=128, B=16,
+                            prior_lens=src.prior_lens, new_lens=src.new_lens, is_chunk=src.is_chunk,
+                            rng=np.random.default_rng(12))
+    ga = runner.prepare(src)
+    runner.store_step(ga)
+    k, v = runner.pack_all(ga)
+    dst = copy.copy(src)
+    dst.free_order = np.random.default_rng(78).permutation(src.num_blocks)
+    gb = runner.prepare(dst, fill=False)
+    slots = runner.all_slots(gb)                 # the receiving side's slots for the same tokens
+    pa.store_kv(gb.cache, k, v, slots)
+    k2, v2 = runner.pack_all(gb)
+    torch.cuda.synchronize()
+    assert torch.equal(k2.view(torch.uint8), k.view(torch.uint8)) and torch.equal(v2.view(torch.uint8), v.view(torch.uint8))
+    oa, ob = runner.decode_step(ga), runner.decode_step(gb)
+    torch.cuda.synchronize()
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
 
 
 # ------------------------------------------------ full sizes, bench launch configuration

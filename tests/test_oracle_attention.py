@@ -8,6 +8,7 @@ quantises through torch's float8_e4m3fn cast.  Closed forms and invariants
 (block permutation, fork before divergence, chunk splitting, split-K merge)
 cover what the dense check cannot see.
 """
+import copy
 import math
 
 import numpy as np
@@ -16,7 +17,7 @@ import torch
 import torch.nn.functional as F
 
 import workloads as W
-from oracle import paged
+from oracle import fp8_e4m3, paged
 from tests import oracle_setup as OS
 
 
@@ -376,3 +377,57 @@ def test_copy_blocks_copies_whole_blocks():
         assert np.array_equal(kc[dd], k0[s]) and np.array_equal(vc[dd], v0[s])
     for b in (0, 1, 3, 4, 5, 6, 8):
         assert np.array_equal(kc[b], k0[b]) and np.array_equal(vc[b], v0[b])
+
+
+# ------------------------------------------------------- pack (KV hand-off)
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
+def test_pack_returns_the_stored_rows_in_token_order(kv):
+    """Packing every sequence gives back, row for row, what was stored: the
+    generator's own values (f32 / bf16) or their e4m3 codes (fp8)."""
+    if kv == "f32":
+        batch = W.config1()
+    elif kv == "bf16":
+        batch = W.config2(small=True)
+    else:
+        batch = W.config3(16, small=True)
+        batch = W.paged_batch("fp8-pack", 9, kv_dtype="fp8", io_dtype="bf16", Hq=8, Hkv=2, d=64, B=16,
+                              prior_lens=batch.prior_lens, new_lens=batch.new_lens, is_chunk=batch.is_chunk,
+                              rng=np.random.default_rng(9))
+    st = OS.build(batch)
+    k, v = paged.pack_kv(st.kc, st.vc, st.tables, batch.total_lens)
+    if kv == "fp8":
+        want_k = fp8_e4m3.quantize(W.bf16_bits_to_f32(batch.k), batch.k_scale[None, :, None])
+        want_v = fp8_e4m3.quantize(W.bf16_bits_to_f32(batch.v), batch.v_scale[None, :, None])
+    else:
+        want_k, want_v = batch.k, batch.v
+    assert k.dtype == st.kc.dtype and k.shape == want_k.shape
+    assert np.array_equal(k, want_k) and np.array_equal(v, want_v)
+
+
+def test_pack_then_store_elsewhere_keeps_attention_bit_identical():
+    """Hand-off round trip: pack from one pool, store into a pool with another
+    block layout (the receiving side's slot mapping), and decode both."""
+    batch = W.config2(small=True)
+    st = OS.build(batch)
+    k, v = paged.pack_kv(st.kc, st.vc, st.tables, batch.total_lens)
+    other = copy.copy(batch)
+    other.free_order = np.random.default_rng(77).permutation(batch.num_blocks)
+    mgr, tables, prior, step, pad = OS.allocate(other)
+    kc, vc = paged.new_pools(other.num_blocks, other.num_kv_heads, other.block_size, other.head_dim, "bf16")
+    slots = np.concatenate([np.concatenate([p, s]) for p, s in zip(prior, step)]).astype(np.int64)
+    paged.store_kv(kc, vc, "bf16", k, v, "bf16", slots)
+    k2, v2 = paged.pack_kv(kc, vc, tables, batch.total_lens)
+    assert np.array_equal(k2, k) and np.array_equal(v2, v)
+    dec = np.flatnonzero(~batch.is_chunk)
+    a = paged.decode_attention(st.kc, st.vc, "bf16", batch.q_decode, "bf16",
+                               OS.table_array([st.tables[i] for i in dec], st.pad_block), batch.total_lens[dec],
+                               batch.scale)
+    b = paged.decode_attention(kc, vc, "bf16", batch.q_decode, "bf16",
+                               OS.table_array([tables[i] for i in dec], pad), batch.total_lens[dec], batch.scale)
+    assert np.array_equal(a, b)
+
+
+def test_pack_of_empty_sequences_is_empty():
+    kc, vc = paged.new_pools(4, 2, 16, 64, "bf16")
+    k, v = paged.pack_kv(kc, vc, [[0], [1, 2]], [0, 0])
+    assert k.shape == (0, 2, 64) and v.shape == (0, 2, 64)
