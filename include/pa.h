@@ -245,6 +245,44 @@ int32_t pa_bm_block_table(const pa_block_manager* bm, int32_t seq, int32_t* tabl
 int32_t pa_bm_used_blocks(const pa_block_manager* bm);
 int32_t pa_bm_ref_count(const pa_block_manager* bm, int32_t block);
 
+/* Prefix cache (serving-stack page, section 4: 前缀缓存, its hash-chain
+ * route and minimal implementation).  Off (capacity 0) on creation.
+ *  - a key names one FULL block of block_size token ids together with the
+ *    key of the block before it, so equal keys mean equal prefixes; keys
+ *    are exact (no digest), so distinct prefixes never share a block;
+ *  - the cache holds one reference of its own on every cached block: a
+ *    cached block outlives the sequences that computed it, stays counted in
+ *    pa_bm_used_blocks, and returns to the free list when it is evicted and
+ *    no sequence holds it;
+ *  - at most capacity_blocks entries; inserting past that evicts the least
+ *    recently used entry (a lookup hit and an insert count as uses; blocks
+ *    of one chain are used front to back, so a chain loses its front first
+ *    and its later entries stop being reachable until the front returns);
+ *  - a lookup that covers at least one block counts as a hit, else a miss.
+ * The token ids are opaque int32 values; they are not stored in the KV
+ * cache and the library never reads device memory here. */
+/* Set the capacity in blocks (0 turns the cache off and evicts every entry;
+ * lowering it evicts least recently used entries down to the new size). */
+int pa_bm_prefix_cache_set_capacity(pa_block_manager* bm, int32_t capacity_blocks);
+/* Longest cached prefix of token_ids (host, [n]): walks its full blocks
+ * front to back and stops at the first one not cached.  Writes up to
+ * max_blocks of the hit's physical blocks to blocks_out (host) and returns
+ * the hit length in tokens (a multiple of block_size). */
+int32_t pa_bm_prefix_lookup(pa_block_manager* bm, const int32_t* token_ids, int32_t n,
+                            int32_t* blocks_out, int32_t max_blocks);
+/* New sequence starting from the longest cached prefix of token_ids: it
+ * shares those blocks (one more reference each) and its length is the hit
+ * (pa_bm_seq_len); the caller appends the remaining tokens with
+ * pa_bm_append, whose first slot opens a new block.  Returns its id. */
+int32_t pa_bm_seq_new_prefixed(pa_block_manager* bm, const int32_t* token_ids, int32_t n);
+/* Record the full blocks of token_ids (host, [n], n <= the sequence's
+ * length: the ids of seq's first n tokens) with seq's block table; blocks
+ * whose key is already cached keep the cached entry.  Returns the number of
+ * entries added. */
+int32_t pa_bm_prefix_insert(pa_block_manager* bm, int32_t seq, const int32_t* token_ids, int32_t n);
+/* out (host, int64[4]) = hits, misses, cached blocks, capacity. */
+int pa_bm_prefix_stats(const pa_block_manager* bm, int64_t* out);
+
 #ifdef __cplusplus
 }
 #endif

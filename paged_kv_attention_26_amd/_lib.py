@@ -59,6 +59,11 @@ SIGNATURES = [
     ("pa_bm_block_table", C.c_int32, [C.c_void_p, _I, _IP, _I]),
     ("pa_bm_used_blocks", C.c_int32, [C.c_void_p]),
     ("pa_bm_ref_count", C.c_int32, [C.c_void_p, _I]),
+    ("pa_bm_prefix_cache_set_capacity", C.c_int, [C.c_void_p, _I]),
+    ("pa_bm_prefix_lookup", C.c_int32, [C.c_void_p, _IP, _I, _IP, _I]),
+    ("pa_bm_seq_new_prefixed", C.c_int32, [C.c_void_p, _IP, _I]),
+    ("pa_bm_prefix_insert", C.c_int32, [C.c_void_p, _I, _IP, _I]),
+    ("pa_bm_prefix_stats", C.c_int, [C.c_void_p, C.POINTER(C.c_int64)]),
 ]
 
 _lib = None

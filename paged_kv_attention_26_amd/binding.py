@@ -283,6 +283,45 @@ class BlockManager:
             raise L.PaError(r, "pa_bm_ref_count")
         return int(r)
 
+    # -- prefix cache (pa_bm_prefix_*) ----------------------------------------
+    @staticmethod
+    def _ids(token_ids):
+        a = np.ascontiguousarray(np.asarray(token_ids, dtype=np.int32).reshape(-1))
+        return a, a.ctypes.data_as(C.POINTER(C.c_int32))
+
+    def set_prefix_capacity(self, capacity_blocks: int) -> None:
+        L.check(self._l.pa_bm_prefix_cache_set_capacity(self._h, int(capacity_blocks)),
+                "pa_bm_prefix_cache_set_capacity")
+
+    def prefix_lookup(self, token_ids):
+        """(hit tokens, physical blocks of the hit)."""
+        a, p = self._ids(token_ids)
+        out = np.zeros(max(len(a) // self.block_size, 1), dtype=np.int32)
+        hit = self._l.pa_bm_prefix_lookup(self._h, p, len(a),
+                                          out.ctypes.data_as(C.POINTER(C.c_int32)), len(out))
+        if hit < 0:
+            raise L.PaError(hit, "pa_bm_prefix_lookup")
+        return int(hit), out[:hit // self.block_size].tolist()
+
+    def seq_new_prefixed(self, token_ids) -> int:
+        a, p = self._ids(token_ids)
+        s = self._l.pa_bm_seq_new_prefixed(self._h, p, len(a))
+        if s < 0:
+            raise L.PaError(s, "pa_bm_seq_new_prefixed")
+        return s
+
+    def prefix_insert(self, seq: int, token_ids) -> int:
+        a, p = self._ids(token_ids)
+        n = self._l.pa_bm_prefix_insert(self._h, seq, p, len(a))
+        if n < 0:
+            raise L.PaError(n, "pa_bm_prefix_insert")
+        return int(n)
+
+    def prefix_stats(self) -> dict:
+        out = (C.c_int64 * 4)()
+        L.check(self._l.pa_bm_prefix_stats(self._h, out), "pa_bm_prefix_stats")
+        return {"hits": out[0], "misses": out[1], "cached_blocks": out[2], "capacity": out[3]}
+
     def unused_block(self) -> int:
         for b in range(self.num_blocks):
             if self._l.pa_bm_ref_count(self._h, b) == 0:

@@ -188,3 +188,62 @@ def fork_decode(gf: GpuFork, device="cuda", out=None, partition_tokens=0, worksp
     lens = np.array([bm.seq_len(b) for b in gf.beams], dtype=np.int32)
     return pa.decode(gf.cache, _t(gf.fb.q, device), table, _t(lens, device), int(lens.max()), gf.fb.scale,
                      out=out, partition_tokens=partition_tokens, workspace=workspace)
+
+
+@dataclass
+class PrefixTurn:
+    active: list             # users taking part, in order
+    hits: list               # tokens each found in the prefix cache
+    tables: list             # block tables after the first reply token
+    prefill_out: torch.Tensor
+    decode_out: torch.Tensor
+
+
+def run_prefix_agent(w, device="cuda"):
+    """Multi-turn conversations through libpa's prefix cache.  Per turn: every
+    active user starts from the longest cached prefix of its prompt, the rest
+    of the prompt is stored and attended as one chunked prefill over the
+    shared blocks, the first reply token is stored and decoded, the rest of
+    the reply is stored, then the prompt and reply are recorded in the cache
+    and the sequence is released.  Returns (cache, block manager, turns)."""
+    bm = pa.BlockManager(w.num_blocks, w.block_size, w.free_order)
+    bm.set_prefix_capacity(w.capacity_blocks)
+    cache = pa.alloc_cache(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, w.kv_dtype,
+                           device=device, k_scale=w.k_scale, v_scale=w.v_scale)
+
+    def store(parts, slots):
+        k = np.concatenate([w.k_rows(u, lo, hi) for u, lo, hi in parts])
+        v = np.concatenate([w.v_rows(u, lo, hi) for u, lo, hi in parts])
+        pa.store_kv(cache, _t(k, device), _t(v, device), _t(np.concatenate(slots).astype(np.int32), device))
+
+    turns = []
+    for t in range(1, w.turns + 1):
+        active = [u for u in range(w.users) if w.join_turn[u] <= t]
+        seqs, hits, lens, slots = [], [], [], []
+        for u in active:
+            n = w.prompt_len(u, t)
+            s = bm.seq_new_prefixed(w.ids(u, 0, n))
+            hit = bm.seq_len(s)
+            slots.append(bm.append(s, n - hit))
+            seqs.append(s), hits.append(hit), lens.append(n)
+        store([(u, h, n) for u, h, n in zip(active, hits, lens)], slots)
+        q_lens = np.array([n - h for h, n in zip(hits, lens)])
+        cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+        q = np.concatenate([w.q_rows(u, h, n) for u, h, n in zip(active, hits, lens)])
+        table = bm.block_tables(seqs, bm.unused_block())
+        out_p = pa.prefill_chunk(cache, _t(q, device), _t(cu, device), _t(np.array(lens, np.int32), device),
+                                 _t(table, device), int(q_lens.max()), max(lens), w.scale).clone()
+        store([(u, n, n + 1) for u, n in zip(active, lens)], [bm.append(s, 1) for s in seqs])
+        table = bm.block_tables(seqs, bm.unused_block())
+        ctx = np.array(lens, np.int32) + 1
+        qd = np.stack([w.q_rows(u, n, n + 1)[0] for u, n in zip(active, lens)])
+        out_d = pa.decode(cache, _t(qd, device), _t(table, device), _t(ctx, device), int(ctx.max()),
+                          w.scale).clone()
+        tables = [bm.block_table(s) for s in seqs]
+        rest = w.reply_len - 1
+        store([(u, n + 1, n + 1 + rest) for u, n in zip(active, lens)], [bm.append(s, rest) for s in seqs])
+        for u, s, n in zip(active, seqs, lens):
+            bm.prefix_insert(s, w.ids(u, 0, n + w.reply_len))
+            bm.release(s)
+        turns.append(PrefixTurn(active, hits, tables, out_p, out_d))
+    return cache, bm, turns

@@ -134,3 +134,63 @@ def fork_decode_ref(fb, st: ForkState):
     lens = np.array([b.length for b in st.beams])
     return paged.decode_attention(st.kc, st.vc, fb.kv_dtype, fb.q, fb.io_dtype, tables, lens, fb.scale,
                                   fb.k_scale, fb.v_scale)
+
+
+@dataclass
+class PrefixTurnRef:
+    active: list
+    hits: list
+    tables: list
+    prefill_out: np.ndarray
+    decode_out: np.ndarray
+
+
+def build_prefix_agent(w):
+    """The oracle's run of the multi-turn prefix-cache conversations, in the
+    same order of decisions as the library's runner: returns (K pool,
+    V pool, manager, cache, turns)."""
+    from oracle.prefix_cache import PrefixCache
+
+    mgr = BlockManager(w.num_blocks, w.block_size, w.free_order)
+    cache = PrefixCache(mgr, w.capacity_blocks)
+    kc, vc = paged.new_pools(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, w.kv_dtype)
+
+    def store(parts, slots):
+        k = np.concatenate([w.k_rows(u, lo, hi) for u, lo, hi in parts])
+        v = np.concatenate([w.v_rows(u, lo, hi) for u, lo, hi in parts])
+        paged.store_kv(kc, vc, w.kv_dtype, k, v, w.io_dtype, np.concatenate(slots).astype(np.int64),
+                       w.k_scale, w.v_scale)
+
+    def pad():
+        return next((b for b in range(w.num_blocks) if mgr.ref_count[b] == 0), 0)
+
+    turns = []
+    for t in range(1, w.turns + 1):
+        active = [u for u in range(w.users) if w.join_turn[u] <= t]
+        seqs, hits, lens, slots = [], [], [], []
+        for u in active:
+            n = w.prompt_len(u, t)
+            s = cache.start(len(turns) * 100 + u, list(w.ids(u, 0, n)))
+            hits.append(s.length)
+            slots.append(s.append_slots(n - s.length))
+            seqs.append(s), lens.append(n)
+        store([(u, h, n) for u, h, n in zip(active, hits, lens)], slots)
+        q_lens = np.array([n - h for h, n in zip(hits, lens)])
+        cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
+        q = np.concatenate([w.q_rows(u, h, n) for u, h, n in zip(active, hits, lens)])
+        out_p = paged.prefill_chunk_attention(kc, vc, w.kv_dtype, q, w.io_dtype, cu, np.array(lens),
+                                              table_array([s.block_table for s in seqs], pad()), w.scale,
+                                              w.k_scale, w.v_scale)
+        store([(u, n, n + 1) for u, n in zip(active, lens)], [s.append_slots(1) for s in seqs])
+        qd = np.stack([w.q_rows(u, n, n + 1)[0] for u, n in zip(active, lens)])
+        out_d = paged.decode_attention(kc, vc, w.kv_dtype, qd, w.io_dtype,
+                                       table_array([s.block_table for s in seqs], pad()),
+                                       np.array(lens) + 1, w.scale, w.k_scale, w.v_scale)
+        tables = [list(s.block_table) for s in seqs]
+        rest = w.reply_len - 1
+        store([(u, n + 1, n + 1 + rest) for u, n in zip(active, lens)], [s.append_slots(rest) for s in seqs])
+        for u, s, n in zip(active, seqs, lens):
+            cache.insert(list(w.ids(u, 0, n + w.reply_len)), s.block_table)
+            s.release()
+        turns.append(PrefixTurnRef(active, hits, tables, out_p, out_d))
+    return kc, vc, mgr, cache, turns

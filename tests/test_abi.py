@@ -214,3 +214,108 @@ def test_native_block_manager_fork_demo():
 def test_native_block_manager_rejects_bad_free_order():
     with pytest.raises(L.PaError):
         NativeBM(4, 16, [0, 1, 1, 3])
+
+
+# ------------------------------------------- native prefix cache == oracle
+def _prefix_trace(seed, steps=200, pool=300, B=16, caps=(3, 8, 40), recaps=(2, 5, 40), alphabet=4):
+    """Drive the native and oracle prefix caches with the same requests:
+    start from the longest cached prefix, append the rest, record, release
+    some, shrink/grow the capacity; compare hits, tables, counts, stats."""
+    from oracle.prefix_cache import PrefixCache
+
+    rng = random.Random(seed)
+    order = np.random.default_rng(seed).permutation(pool)
+    o = OracleBM(pool, B, order)
+    n = NativeBM(pool, B, order)
+    cap = rng.choice(caps)
+    oc = PrefixCache(o, cap)
+    n.set_prefix_capacity(cap)
+    stems = [[rng.randrange(alphabet) for _ in range(rng.randint(0, 100))] for _ in range(5)]
+    live = []
+    for step in range(steps):
+        r = rng.random()
+        if r < 0.05:
+            cap = rng.choice(recaps)
+            while len(oc.table) > cap:              # the oracle's own LRU order
+                victim, _ = oc.lru.popitem(last=False)
+                o.free(oc.table.pop(victim))
+            oc.capacity = cap
+            n.set_prefix_capacity(cap)
+        elif r < 0.15:
+            toks = list(rng.choice(stems)) + [rng.randrange(3) for _ in range(rng.randint(0, 30))]
+            assert n.prefix_lookup(toks) == tuple(oc.lookup(toks))
+        else:
+            toks = list(rng.choice(stems)) + [rng.randrange(3) for _ in range(rng.randint(0, 50))]
+            os_ = oc.start(step, toks)
+            ns = n.seq_new_prefixed(toks)
+            assert n.seq_len(ns) == os_.length
+            assert n.block_table(ns) == os_.block_table
+            extra = len(toks) - os_.length
+            if len(o.free_ids) < extra // B + 2:
+                os_.release(), n.release(ns)
+            else:
+                assert n.append(ns, extra).tolist() == os_.append_slots(extra)
+                assert n.prefix_insert(ns, toks) == oc.insert(toks, os_.block_table)
+                live.append((os_, ns))
+        if len(live) > 5:
+            a, b = live.pop(rng.randrange(len(live)))
+            a.release(), n.release(b)
+        assert [n.ref_count(b) for b in range(pool)] == o.ref_count
+        assert n.used_blocks == o.used_blocks
+        st = n.prefix_stats()
+        assert (st["hits"], st["misses"], st["cached_blocks"], st["capacity"]) == \
+            (oc.hits, oc.misses, len(oc.table), oc.capacity)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_native_prefix_cache_matches_oracle(seed):
+    _prefix_trace(seed)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_native_prefix_cache_matches_oracle_at_tiny_capacity(seed):
+    # Capacities of 1-4 blocks over a 2-symbol alphabet: chains lose their
+    # front often, so recorded blocks often sit under keys whose parent is
+    # no longer cached (the case where an eviction walks up the chain).
+    _prefix_trace(100 + seed, caps=(1, 2, 3), recaps=(1, 2, 4), alphabet=2)
+
+
+def test_native_prefix_cache_agent_turns():
+    """Multi-turn agent example (serving-stack page, section 4.3), prompt
+    and reply recorded each turn: hit_t = 16 floor((|prompt_(t-1)| + 120) / 16)."""
+    n = NativeBM(4096, 16)
+    n.set_prefix_capacity(4096)
+    history = list(range(1000))
+    for t in range(1, 8):
+        user = list(range(90000 + t * 100, 90000 + t * 100 + 60))
+        reply = list(range(80000 + t * 50, 80000 + t * 50 + 120))
+        prompt = history + user
+        s = n.seq_new_prefixed(prompt)
+        hit = n.seq_len(s)
+        assert hit == (0 if t == 1 else 16 * ((1060 + 180 * (t - 2) + 120) // 16))
+        n.append(s, len(prompt) + len(reply) - hit)
+        n.prefix_insert(s, prompt + reply)
+        n.release(s)
+        history = prompt + reply
+    st = n.prefix_stats()
+    assert (st["hits"], st["misses"]) == (6, 1)
+    assert st["cached_blocks"] == n.used_blocks == (1000 + 7 * 180) // 16
+
+
+def test_native_prefix_cache_rejects_bad_arguments():
+    n = NativeBM(8, 16)
+    with pytest.raises(L.PaError):
+        n.prefix_lookup([1] * 16)                 # off until a capacity is set
+    with pytest.raises(L.PaError):
+        n.set_prefix_capacity(-1)
+    n.set_prefix_capacity(4)
+    s = n.seq_new()
+    n.append(s, 16)
+    with pytest.raises(L.PaError):
+        n.prefix_insert(s, [0] * 17)              # more ids than the sequence holds
+    with pytest.raises(L.PaError):
+        n.prefix_insert(99, [0] * 16)
+    assert n.prefix_insert(s, [0] * 16) == 1
+    assert n.prefix_insert(s, [0] * 16) == 0      # already cached
+    n.set_prefix_capacity(0)                      # off again: evicts every entry
+    assert n.ref_count(n.block_table(s)[0]) == 1

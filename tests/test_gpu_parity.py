@@ -433,3 +433,29 @@ def test_verify_full_batch():
     err = np.max(np.abs(got - OS.chunk_ref(batch, OS.build(batch))))
     say(f"      max abs err {err:.3e}")
     assert err < TOL["bf16"]
+
+
+@pytest.mark.parametrize("kv,small", [("bf16", True), ("fp8", True), ("bf16", False)])
+def test_prefix_cache_conversations(kv, small):
+    """Multi-turn conversations sharing a system prompt through the prefix
+    cache: the library's block manager takes the oracle's decisions, chunked
+    prefill and decode over the shared blocks match the oracle, and the
+    blocks the cache holds at the end are bit-identical."""
+    from paged_kv_attention_26_amd import runner
+    w = W.prefix_agent(small=small, kv_dtype=kv)
+    say(f"[gpu] prefix cache {w.name}")
+    cache, bm, got = runner.run_prefix_agent(w)
+    torch.cuda.synchronize()
+    kc, vc, mgr, oc, ref = OS.build_prefix_agent(w)
+    for t, (g, r) in enumerate(zip(got, ref), start=1):
+        assert g.active == r.active and g.hits == r.hits and g.tables == r.tables, t
+        ep = np.max(np.abs(out_f64(g.prefill_out) - r.prefill_out))
+        ed = np.max(np.abs(out_f64(g.decode_out) - r.decode_out))
+        say(f"      turn {t}: hits {g.hits} prefill err {ep:.3e} decode err {ed:.3e}")
+        assert ep < TOL[kv] and ed < TOL[kv]
+    st = bm.prefix_stats()
+    assert (st["hits"], st["misses"], st["cached_blocks"]) == (oc.hits, oc.misses, len(oc.table))
+    held = sorted(oc.table.values())
+    assert held == [b for b in range(w.num_blocks) if bm.ref_count(b)]
+    assert np.array_equal(bits(cache.k_cache, kv)[held], oracle_bits(kc, kv)[held])
+    assert np.array_equal(bits(cache.v_cache, kv)[held], oracle_bits(vc, kv)[held])

@@ -288,3 +288,114 @@ def chunk_tokens_of(batch: PagedBatch):
     """Helpers for laying out step inputs: per-sequence slices into k / v."""
     off = batch.tok_offsets
     return [(int(off[i]), int(batch.prior_lens[i]), int(batch.new_lens[i])) for i in range(batch.num_seqs)]
+
+
+@dataclass
+class PrefixAgent:
+    """Multi-turn agent conversations sharing one system prompt, for the
+    prefix cache: every user's prompt at its local turn tau is the system
+    prompt, the user's whole history of (message, reply) pairs, then a new
+    message; after it, a reply is generated.  Users join at ``join_turn``.
+
+    Token ids: the system prompt is 0..sys_len-1; user u's own tokens are
+    ``1_000_000 (u + 1) + i`` for i along its conversation.  K, V and Q rows
+    are drawn per token position of each user's stream; system-prompt
+    positions take the shared rows, so equal token prefixes carry equal K/V.
+    """
+    name: str
+    seed: int
+    kv_dtype: str
+    io_dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    free_order: np.ndarray
+    capacity_blocks: int
+    sys_len: int
+    user_len: int
+    reply_len: int
+    turns: int
+    join_turn: list          # per user, first turn (1-based) it takes part in
+    k_sys: np.ndarray        # [sys_len, Hkv, d]
+    v_sys: np.ndarray
+    k_conv: np.ndarray       # [users, conv_len, Hkv, d]
+    v_conv: np.ndarray
+    q_all: np.ndarray        # [users, sys_len + conv_len, Hq, d]
+    k_scale: Optional[np.ndarray] = None
+    v_scale: Optional[np.ndarray] = None
+    scale: float = 0.0
+
+    @property
+    def users(self) -> int:
+        return len(self.join_turn)
+
+    @property
+    def turn_len(self) -> int:
+        return self.user_len + self.reply_len
+
+    def local_turn(self, u: int, t: int) -> int:
+        return t - self.join_turn[u] + 1
+
+    def prompt_len(self, u: int, t: int) -> int:
+        return self.sys_len + (self.local_turn(u, t) - 1) * self.turn_len + self.user_len
+
+    def ids(self, u: int, lo: int, hi: int) -> np.ndarray:
+        pos = np.arange(lo, hi, dtype=np.int64)
+        own = 1_000_000 * (u + 1) + (pos - self.sys_len)
+        return np.where(pos < self.sys_len, pos, own).astype(np.int32)
+
+    def _rows(self, shared, own, u, lo, hi):
+        parts = []
+        if lo < self.sys_len:
+            parts.append(shared[lo:min(hi, self.sys_len)])
+        if hi > self.sys_len:
+            parts.append(own[u, max(lo, self.sys_len) - self.sys_len:hi - self.sys_len])
+        return np.concatenate(parts) if parts else shared[:0]
+
+    def k_rows(self, u, lo, hi):
+        return self._rows(self.k_sys, self.k_conv, u, lo, hi)
+
+    def v_rows(self, u, lo, hi):
+        return self._rows(self.v_sys, self.v_conv, u, lo, hi)
+
+    def q_rows(self, u, lo, hi):
+        return self.q_all[u, lo:hi]
+
+
+def prefix_agent(small=False, kv_dtype="bf16") -> PrefixAgent:
+    """The multi-turn agent example of the serving stack's prefix-cache
+    section: a 1000-token system prompt, 60-token user messages, 120-token
+    replies, 7 turns, 16-token blocks, a 4096-block cache; here four users
+    start together and a fifth joins at turn 2 (Qwen3-8B layer shapes).
+    ``small``: 100 / 12 / 20 tokens, 3 turns, 2 + 1 users, 8 / 2 heads."""
+    seed = 7 if not small else 107
+    rng = np.random.default_rng(seed)
+    if small:
+        sys_len, user_len, reply_len, turns, join = 100, 12, 20, 3, [1, 1, 2]
+        Hq, Hkv, d = 8, 2, 128
+    else:
+        sys_len, user_len, reply_len, turns, join = 1000, 60, 120, 7, [1, 1, 1, 1, 2]
+        Hq, Hkv, d = 32, 8, 128
+    B, cap = 16, 4096
+    conv_len = turns * (user_len + reply_len)
+    U = len(join)
+    # Room for every user's whole stream twice over (turn-1 prompts are
+    # computed before any of them is recorded, so the system prompt is held
+    # U times at once), plus slack.
+    nb = int(math.ceil(2 * U * math.ceil((sys_len + conv_len) / B))) + 8
+    free_order = rng.permutation(nb).astype(np.int64)
+    k_sys = _values(rng, (sys_len, Hkv, d), "bf16")
+    v_sys = _values(rng, (sys_len, Hkv, d), "bf16")
+    k_conv = _values(rng, (U, conv_len, Hkv, d), "bf16")
+    v_conv = _values(rng, (U, conv_len, Hkv, d), "bf16")
+    q_all = _values(rng, (U, sys_len + conv_len, Hq, d), "bf16")
+    ks = vs = None
+    if kv_dtype == "fp8":
+        ks, vs = _head_scales(np.concatenate([k_sys, k_conv.reshape(-1, Hkv, d)]),
+                              np.concatenate([v_sys, v_conv.reshape(-1, Hkv, d)]))
+    name = f"prefix-agent-{kv_dtype}" + ("-small" if small else "")
+    return PrefixAgent(name, seed, kv_dtype, "bf16", Hq, Hkv, d, B, nb, free_order, cap, sys_len, user_len,
+                       reply_len, turns, join, k_sys, v_sys, k_conv, v_conv, q_all, ks, vs,
+                       float(np.float32(1.0 / math.sqrt(d))))
