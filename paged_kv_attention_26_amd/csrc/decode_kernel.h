@@ -151,15 +151,20 @@ __device__ __forceinline__ float xload(const float* p) {
 // Count this wave in on up to two split items (counter c[i], n[i] waves
 // each); last[i] is true for the last of an item's waves to arrive, which then
 // owns its merge and leaves the counter at zero for the next call.  Both
-// increments go out before either result is awaited.
-__device__ __forceinline__ void arrive_last2(int32_t* c0, int n0, bool h0, int32_t* c1, int n1, bool h1,
-                                             bool& last0, bool& last1) {
+// increments go out before either result is awaited.  early0: this wave
+// already added itself to c0 (with no result); it only reads c0, and merges
+// when the count is complete.
+__device__ __forceinline__ void arrive_last2(int32_t* c0, int n0, bool h0, bool early0, int32_t* c1, int n1,
+                                             bool h1, bool& last0, bool& last1) {
   int r0 = 0, r1 = 0;
   const bool l0 = (threadIdx.x & 63) == 0;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0x0F70);                      // this wave's partial stores are complete
   __builtin_amdgcn_sched_barrier(0);
-  if (l0 && h0) r0 = __hip_atomic_fetch_add(c0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (l0 && h0) {
+    if (early0) r0 = __hip_atomic_load(c0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - 1;
+    else r0 = __hip_atomic_fetch_add(c0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (l0 && h1) r1 = __hip_atomic_fetch_add(c1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   r0 = __builtin_amdgcn_readfirstlane(r0);
   r1 = __builtin_amdgcn_readfirstlane(r1);
@@ -185,7 +190,7 @@ __device__ __forceinline__ void merge_split(const DecodeArgs& a, int seq, int kv
 #pragma unroll
     for (int k = 0; k < PL; ++k) o[g][k] = 0.f;
   }
-  constexpr int NB = G <= 4 ? 4 : 2;                       // partials whose loads are in flight at once
+  constexpr int NB = G <= 4 ? 8 : 2;                       // partials whose loads are in flight at once
   for (int i0 = 0; i0 < n; i0 += NB) {
     float m[NB][G], l[NB][G], x[NB][G][PL];
 #pragma unroll
@@ -336,11 +341,16 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
 
   LoadT kreg[C::BPC][C::KLB];
   LoadT vreg[C::BPC][C::VLB];
+  // Bytes of a tile that the next loads may read: a whole tile while the
+  // cursor is live, none past the range's last step.  Loads through an empty
+  // descriptor return zeros without a memory access, so the wait that closes
+  // the range has no tile in flight to wait for.
+  uint32_t nx_bytes = uint32_t(kTile);
   auto load_k = [&](const int (&ids)[C::BPC], int kh) {
 #pragma unroll
     for (int k = 0; k < C::BPC; ++k) {
       const auto r = tile_rsrc(kpool + (uint64_t(uint32_t(ids[k])) * uint32_t(Hkv) + uint32_t(kh)) * kTile,
-                               uint32_t(kTile));
+                               nx_bytes);
 #pragma unroll
       for (int i = 0; i < C::KLB; ++i) buffer_load(r, k_off, uint32_t(i * C::RPL * D * C::ES), kreg[k][i]);
     }
@@ -349,7 +359,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
 #pragma unroll
     for (int k = 0; k < C::BPC; ++k) {
       const auto r = tile_rsrc(vpool + (uint64_t(uint32_t(ids[k])) * uint32_t(Hkv) + uint32_t(kh)) * kTile,
-                               uint32_t(kTile));
+                               nx_bytes);
 #pragma unroll
       for (int j = 0; j < C::VLB; ++j) buffer_load(r, v_off, uint32_t(j * C::DPL * B * C::ES), vreg[k][j]);
     }
@@ -407,6 +417,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
   advance(nx);
   cursor_ids(nx, ids_nx);
   kvh_nx = nx.kvh;
+  nx_bytes = nx.live ? uint32_t(kTile) : 0u;
 
   // Split items this wave holds a partial of (at most two: the first and the
   // last of its range).  It counts itself in on them only once its whole range
@@ -417,6 +428,15 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
   };
   Pending pend[2] = {{0, 0, 0, 1, 0, false}, {0, 0, 0, 1, 0, false}};
   bool has_pend[2] = {false, false};
+  // A range's first item, when split and followed by more of the range, is
+  // counted in on as soon as its partial is stored, with an add whose result
+  // nobody waits for: the neighbour that finishes the item later usually
+  // merges it, not this wave, which still has the rest of its range to
+  // stream.  After its range this wave reads the counter: if it shows every
+  // wave of the item, the wave merges too (a merge by two waves writes the
+  // same bits twice; no merge is ever missed, since the wave whose add
+  // completes the count also merges).
+  bool early = false;
 
   bool first = true;
   bool q_ready = false;                                      // qfn / qpn hold this segment's query
@@ -606,6 +626,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
       advance(nx);                                            // ids one step ahead of their loads
       cursor_ids(nx, ids_nx);
       kvh_nx = nx.kvh;
+      nx_bytes = nx.live ? uint32_t(kTile) : 0u;
     };
     for (int st = 0; st + 1 < nsteps; ++st) do_step(st, std::false_type{});
     q_ready = nsteps > 0;
@@ -661,6 +682,13 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
       const int w1 = owner_wave(u0 + nu - 1, U, W);
       pend[slot] = Pending{seq, kvh, w0, w1 - w0 + 1, w1, int64_t(w0) * U / W == u0};
       has_pend[slot] = true;
+      if (slot == 0 && u + (p_end - part) < u_end) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0x0F70);                 // the partial stores are complete
+        __builtin_amdgcn_sched_barrier(0);
+        if (lane == 0) __hip_atomic_fetch_add(a.arrivals + w1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        early = true;
+      }
     }
 
     u += p_end - part;
@@ -676,8 +704,8 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
   // Count in on the split items; the last wave to arrive at one merges it.
   if (has_pend[0] || has_pend[1]) {
     bool last0, last1;
-    arrive_last2(a.arrivals + pend[0].w1, pend[0].n, has_pend[0], a.arrivals + pend[1].w1, pend[1].n, has_pend[1],
-                 last0, last1);
+    arrive_last2(a.arrivals + pend[0].w1, pend[0].n, has_pend[0], early, a.arrivals + pend[1].w1, pend[1].n,
+                 has_pend[1], last0, last1);
     if (last0) merge_split<D, G, C::F32>(a, pend[0].seq, pend[0].kvh, pend[0].w0, pend[0].n, pend[0].w0_first);
     if (last1) merge_split<D, G, C::F32>(a, pend[1].seq, pend[1].kvh, pend[1].w0, pend[1].n, pend[1].w0_first);
   }
