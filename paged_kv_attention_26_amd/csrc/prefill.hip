@@ -28,9 +28,9 @@
 //    block, so its A operand (8 consecutive keys of one head dimension) is
 //    one 16-byte load.
 //  * Online softmax in base 2 with the scale folded into exp2's argument
-//    (the hardware v_exp_f32: arguments are <= 0, results that would be
-//    denormal flush to zero, far below bf16 resolution of the sum);
-//    O^T is rescaled only when some column's running max grows.
+//    (the hardware v_exp_f32; results that would be denormal flush to zero,
+//    far below bf16 resolution of the sum); O^T is rescaled only when some
+//    column's running max grows by more than 2^8 (probabilities stay <= 256).
 //  * The causal mask is applied only on key tiles that reach the diagonal;
 //    keys past the sequence are masked by select and their V rows zeroed,
 //    so NaN in unused slots never reaches the result.
@@ -146,27 +146,34 @@ __global__ void __launch_bounds__(kPrefillWaves * 64) prefill_kernel(PrefillArgs
   // vd, 8-key group vkc).  Keys past the workgroup's range re-read its last
   // key (their scores are masked, their V zeroed).
   static_assert(kPrefillWaves * 64 == KT * 16 && kPrefillWaves * 64 == D * 4, "one chunk of K and V per thread");
+  static_assert(B == KT || 2 * B == KT, "a tile is one or two blocks");
   const int kr = tid >> 4, kcc = tid & 15;
   const int vd = tid >> 2, vkc = tid & 3;
+  // Per-thread constants: the chunk's offset inside its block's tile, which
+  // of the tile's two blocks holds it (block 16: keys 16..31 and 8-key
+  // groups 2, 3), and its LDS address.  A tile past the last key reads the
+  // last block again (tile_ids clamps), so every address stays inside an
+  // allocated block; those keys are masked.
+  constexpr uint64_t kBlockTile = uint64_t(B) * D * ES;    // bytes of one (block, kv head) tile
+  const uint64_t k_lane = uint64_t(((kr % B) * D + kcc * 8) * ES);
+  const uint64_t v_lane = uint64_t((vd * B + (8 * vkc) % B) * ES);
+  const bool k_hi = B != KT && kr >= B;
+  const bool v_hi = B != KT && 8 * vkc >= B;
+  const int k_lds = kr * KROW + (kcc ^ kswz(kr)) * 16;
+  const int v_lds = KBUF + vd * VROW + vkc * 16;
   // (macros over plain variables: two staging sets, kept in registers)
-#define PA_STAGE_LOAD(P, KT_, ID0, ID1)                                                                           \
-  do {                                                                                                        \
-    const int k0_ = (KT_) * KT;                                                                               \
-    const int b0_ = k0_ / B;                                                                                  \
-    const int key_ = min(k0_ + kr, kmax);                                                                     \
-    const int bk_ = key_ / B == b0_ ? (ID0) : (ID1);                                                          \
-    P##k = *reinterpret_cast<const typename Raw::T*>(kpool + ((size_t(bk_) * Hkv + kvh) * B + key_ % B) *     \
-                                                     (D * ES) + kcc * 8 * ES);                                \
-    const int kb_ = min(k0_ + 8 * vkc, kmax & ~7);                                                            \
-    const int bv_ = kb_ / B == b0_ ? (ID0) : (ID1);                                                           \
-    P##v = *reinterpret_cast<const typename Raw::T*>(vpool + ((size_t(bv_) * Hkv + kvh) * D + vd) * (B * ES) + \
-                                                     (kb_ % B) * ES);                                         \
+#define PA_STAGE_LOAD(P, KT_, ID0, ID1)                                                                   \
+  do {                                                                                                \
+    const uint64_t t0_ = (uint64_t(uint32_t(ID0)) * uint32_t(Hkv) + uint32_t(kvh)) * kBlockTile;       \
+    const uint64_t t1_ = (uint64_t(uint32_t(ID1)) * uint32_t(Hkv) + uint32_t(kvh)) * kBlockTile;       \
+    P##k = *reinterpret_cast<const typename Raw::T*>(kpool + (k_hi ? t1_ : t0_) + k_lane);            \
+    P##v = *reinterpret_cast<const typename Raw::T*>(vpool + (v_hi ? t1_ : t0_) + v_lane);            \
   } while (0)
-#define PA_STAGE_STORE(P, BUF)                                                                                \
-  do {                                                                                                        \
-    char* sb_ = smem[BUF];                                                                                    \
-    *reinterpret_cast<uint4*>(sb_ + kr * KROW + (kcc ^ kswz(kr)) * 16) = Raw::to_bf16(P##k);                  \
-    *reinterpret_cast<uint4*>(sb_ + KBUF + vd * VROW + vkc * 16) = Raw::to_bf16(P##v);                        \
+#define PA_STAGE_STORE(P, BUF)                                                                        \
+  do {                                                                                                \
+    char* sb_ = smem[BUF];                                                                            \
+    *reinterpret_cast<uint4*>(sb_ + k_lds) = Raw::to_bf16(P##k);                                      \
+    *reinterpret_cast<uint4*>(sb_ + v_lds) = Raw::to_bf16(P##v);                                      \
   } while (0)
   // block ids of a tile's (at most two) blocks, read through the scalar cache
   auto tile_ids = [&](int kt, int& id0, int& id1) __attribute__((always_inline)) {
@@ -206,6 +213,10 @@ __global__ void __launch_bounds__(kPrefillWaves * 64) prefill_kernel(PrefillArgs
       f32x16_t sc = f32x16_t{};
 #pragma unroll
       for (int st = 0; st < 8; ++st) sc = mfma32(ka[st], qb[st], sc);
+      // all eight operand reads go out before the first MFMA: one wait
+      // instead of one per pair
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 
       // accumulator r = 4i + j holds MFMA row 8i + 4hh + j, i.e. key k0 + swap23(8i + 4hh + j)
       if (k0 + KT - 1 > first_row_pos) {                 // tile reaches the diagonal or the end
@@ -220,7 +231,13 @@ __global__ void __launch_bounds__(kPrefillWaves * 64) prefill_kernel(PrefillArgs
       for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       const float m_new = fmaxf(m_run, mt);
-      if (__any(m_new > m_run)) {
+      // O^T and l are rescaled only when some column's maximum grew by more
+      // than 2^8 in exp2 units: until then the stale maximum keeps every
+      // probability <= 256, which bf16 and fp32 hold at full relative
+      // precision, and the final division by l is unchanged.  The first tile
+      // always rescales (m_run = -inf), and it holds key 0, unmasked in
+      // every column, so m_run is finite from then on.
+      if (__any((m_new - m_run) * c > 8.f)) {
         const float al = __builtin_amdgcn_exp2f((m_run - m_new) * c);
         l_run *= al;
 #pragma unroll
