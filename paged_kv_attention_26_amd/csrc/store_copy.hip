@@ -117,79 +117,125 @@ __global__ void __launch_bounds__(256) copy_blocks_kernel(CopyArgs a) {
   }
 }
 
-// One workgroup = one (block, kv head) tile of one sequence.  K rows leave as
-// they are (16-byte chunks, contiguous on both sides); the transposed V tile
-// goes through LDS and leaves as token rows.
+// One (block, kv head) tile: block index bi of sequence seq's table.  K rows
+// leave as they are (16-byte chunks, contiguous on both sides); the
+// transposed V tile goes through LDS and leaves as token rows.
 template <int ES>
-__global__ void __launch_bounds__(256) pack_kv_kernel(PackArgs a) {
+__device__ __forceinline__ void pack_tile(const PackArgs& a, int seq, int bi, int h, char* s_v) {
   constexpr int EPC = 16 / ES;                             // elements per 16-byte chunk
-  __shared__ __attribute__((aligned(16))) char s_v[32 * 128 * ES];   // [token][dim], at most B 32 x d 128
-  const int seq = blockIdx.x, bi = blockIdx.y, h = blockIdx.z;
+  constexpr int NI = (ES == 1) ? 1 : (ES == 2 ? 2 : 4);   // chunks per thread at most (block 32, d 128)
   const int H = a.num_kv_heads, D = a.head_dim, BS = a.block_size;
   const int L = a.seq_lens[seq];
-  if (bi * BS >= L) return;                                // whole workgroup
-  const int ntok = min(BS, L - bi * BS);
+  const int ntok = min(BS, L - bi * BS);                   // >= 1: the tile is a used block
   const int blk = a.block_table[size_t(seq) * a.max_blocks_per_seq + bi];
   const size_t row0 = size_t(a.cu_rows[seq]) + size_t(bi) * BS;
   const int cpr = D / EPC;                                 // 16-byte chunks per token row
   const int cpv = BS / EPC;                                // 16-byte chunks per transposed V row
-  const char* kc = static_cast<const char*>(a.k_cache);
-  const char* vc = static_cast<const char*>(a.v_cache);
+  const char* ktile = static_cast<const char*>(a.k_cache) + (size_t(blk) * H + h) * size_t(BS) * D * ES;
+  const char* vtile = static_cast<const char*>(a.v_cache) + (size_t(blk) * H + h) * size_t(D) * BS * ES;
   char* ko = static_cast<char*>(a.k_out);
   char* vo = static_cast<char*>(a.v_out);
-  // every load of the thread goes out before its first store
-  const char* ktile = kc + (size_t(blk) * H + h) * size_t(BS) * D * ES;
-  const char* vtile = vc + (size_t(blk) * H + h) * size_t(D) * BS * ES;
   const int nk = ntok * cpr, nv = D * cpv;
-  // (loads are unconditional, clamped to the last chunk, so that they stay
-  // in registers and all fly together; only the stores are guarded)
-  constexpr int NI = (ES == 1) ? 1 : (ES == 2 ? 2 : 4);   // chunks per thread at most (block 32, d 128)
-  uint4 kx[NI], vx[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int c = min(int(threadIdx.x) + 256 * i, nk - 1);
-    kx[i] = *reinterpret_cast<const uint4*>(ktile + (size_t(c / cpr) * D) * ES + (c % cpr) * 16);
+  // every load of the thread goes out before its first store.  Loads are
+  // unconditional, clamped to the last chunk, so that they all fly
+  // together; only the stores are guarded.
+  // (chunks in plain named registers: no array or lambda capture, which
+  // inside the tile loop would go to private memory)
+  uint4 k0{}, k1{}, k2{}, k3{}, v0{}, v1{}, v2{}, v3{};
+#define PA_PK_LOAD(I)                                                                                     \
+  if constexpr (NI > I) {                                                                                 \
+    const int ck = min(int(threadIdx.x) + 256 * I, nk - 1);                                              \
+    k##I = *reinterpret_cast<const uint4*>(ktile + (size_t(ck / cpr) * D) * ES + (ck % cpr) * 16);        \
+    const int cv = min(int(threadIdx.x) + 256 * I, nv - 1);                                              \
+    v##I = *reinterpret_cast<const uint4*>(vtile + (size_t(cv / cpv) * BS + (cv % cpv) * EPC) * ES);     \
   }
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int c = min(int(threadIdx.x) + 256 * i, nv - 1);
-    vx[i] = *reinterpret_cast<const uint4*>(vtile + (size_t(c / cpv) * BS + (c % cpv) * EPC) * ES);
+#define PA_PK_STORE(I)                                                                                    \
+  if constexpr (NI > I) {                                                                                 \
+    const int c = threadIdx.x + 256 * I;                                                                  \
+    if (c < nk)                                                                                           \
+      *reinterpret_cast<uint4*>(ko + ((row0 + c / cpr) * H + h) * size_t(D) * ES + (c % cpr) * 16) = k##I; \
+    if (c < nv) {                                                                                         \
+      const int dim = c / cpv, t0 = (c % cpv) * EPC;                                                      \
+      const uint32_t w_[4] = {v##I.x, v##I.y, v##I.z, v##I.w};                                            \
+      _Pragma("unroll") for (int e = 0; e < EPC; ++e) {                                                   \
+        char* dst = s_v + (size_t(t0 + e) * D + dim) * ES;                                                \
+        if constexpr (ES == 4) *reinterpret_cast<uint32_t*>(dst) = w_[e];                                 \
+        else if constexpr (ES == 2) *reinterpret_cast<uint16_t*>(dst) = uint16_t(w_[e >> 1] >> (16 * (e & 1))); \
+        else *reinterpret_cast<uint8_t*>(dst) = uint8_t(w_[e >> 2] >> (8 * (e & 3)));                    \
+      }                                                                                                   \
+    }                                                                                                     \
   }
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    if (c < nk)
-      *reinterpret_cast<uint4*>(ko + ((row0 + c / cpr) * H + h) * size_t(D) * ES + (c % cpr) * 16) = kx[i];
-  }
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {                           // transpose [dim][token] -> [token][dim]
-    const int c = threadIdx.x + 256 * i;
-    if (c >= nv) continue;
-    const int dim = c / cpv, t0 = (c % cpv) * EPC;
-    const uint32_t w[4] = {vx[i].x, vx[i].y, vx[i].z, vx[i].w};
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      char* dst = s_v + (size_t(t0 + e) * D + dim) * ES;
-      if constexpr (ES == 4) *reinterpret_cast<uint32_t*>(dst) = w[e];
-      else if constexpr (ES == 2) *reinterpret_cast<uint16_t*>(dst) = uint16_t(w[e >> 1] >> (16 * (e & 1)));
-      else *reinterpret_cast<uint8_t*>(dst) = uint8_t(w[e >> 2] >> (8 * (e & 3)));
-    }
-  }
+  PA_PK_LOAD(0) PA_PK_LOAD(1) PA_PK_LOAD(2) PA_PK_LOAD(3)
+  PA_PK_STORE(0) PA_PK_STORE(1) PA_PK_STORE(2) PA_PK_STORE(3)
+#undef PA_PK_LOAD
+#undef PA_PK_STORE
   __syncthreads();
   for (int c = threadIdx.x; c < nk; c += 256) {
     const int tok = c / cpr, cc = c % cpr;
     *reinterpret_cast<uint4*>(vo + ((row0 + tok) * H + h) * size_t(D) * ES + cc * 16) =
         *reinterpret_cast<const uint4*>(s_v + (size_t(tok) * D) * ES + cc * 16);
   }
+  __syncthreads();                                         // s_v is rewritten by the next tile
+}
+
+// Tiles are (block, kv head) pairs of the sequences' used blocks (at most
+// max_blocks_used per sequence, the blocks of max_seq_len), numbered
+// sequence by sequence, block by block, kv head fastest (the heads of one
+// block are neighbours in both caches).  Each workgroup first lays out, in
+// LDS, the prefix of used blocks over the sequences, then walks the tiles
+// with a grid-sized stride: no workgroup is launched for a block past a
+// sequence's end.
+template <int ES>
+__global__ void __launch_bounds__(256) pack_kv_kernel(PackArgs a, int num_seqs, int max_blocks_used) {
+  __shared__ __attribute__((aligned(16))) char s_v[32 * 128 * ES];   // [token][dim], at most B 32 x d 128
+  __shared__ int s_tmp[256];
+  extern __shared__ int s_pre[];                           // [num_seqs + 1] used blocks before each sequence
+  const int S = num_seqs;
+  const int H = a.num_kv_heads, BS = a.block_size;
+  {
+    const int per = (S + 255) / 256;
+    const int i0 = threadIdx.x * per, i1 = min(S, i0 + per);
+    int local = 0;
+    for (int i = i0; i < i1; ++i) local += min((max(0, a.seq_lens[i]) + BS - 1) / BS, max_blocks_used);
+    s_tmp[threadIdx.x] = local;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int v = int(threadIdx.x) >= off ? s_tmp[threadIdx.x - off] : 0;
+      __syncthreads();
+      s_tmp[threadIdx.x] += v;
+      __syncthreads();
+    }
+    int run = threadIdx.x ? s_tmp[threadIdx.x - 1] : 0;
+    for (int i = i0; i < i1; ++i) {
+      s_pre[i] = run;
+      run += min((max(0, a.seq_lens[i]) + BS - 1) / BS, max_blocks_used);
+    }
+    if (threadIdx.x == 255) s_pre[S] = s_tmp[255];
+    __syncthreads();
+  }
+  const int64_t tiles = int64_t(s_pre[S]) * H;
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const int tb = int(tile / H), h = int(tile - int64_t(tb) * H);
+    int lo = 0, hi = S;                                    // largest seq with s_pre[seq] <= tb
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pre[mid] <= tb) lo = mid; else hi = mid;
+    }
+    pack_tile<ES>(a, lo, tb - s_pre[lo], h, s_v);
+  }
 }
 
 hipError_t launch_pack_kv(const PackArgs& a, int es, int num_seqs, int max_blocks_used, hipStream_t s) {
   if (num_seqs == 0 || max_blocks_used == 0) return hipSuccess;
-  dim3 grid(num_seqs, max_blocks_used, a.num_kv_heads);
+  // enough workgroups to fill the chip several times over, never more than
+  // the tiles there can be
+  const int64_t upper = int64_t(num_seqs) * max_blocks_used * a.num_kv_heads;
+  const int64_t wgs = upper < 8192 ? upper : 8192;
+  const size_t lds = size_t(num_seqs + 1) * sizeof(int);
   switch (es) {
-    case 4: hipLaunchKernelGGL(pack_kv_kernel<4>, grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(pack_kv_kernel<2>, grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL(pack_kv_kernel<1>, grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(pack_kv_kernel<4>, dim3(uint32_t(wgs)), dim3(256), lds, s, a, num_seqs, max_blocks_used); break;
+    case 2: hipLaunchKernelGGL(pack_kv_kernel<2>, dim3(uint32_t(wgs)), dim3(256), lds, s, a, num_seqs, max_blocks_used); break;
+    default: hipLaunchKernelGGL(pack_kv_kernel<1>, dim3(uint32_t(wgs)), dim3(256), lds, s, a, num_seqs, max_blocks_used); break;
   }
   return hipGetLastError();
 }
