@@ -9,14 +9,16 @@
 //
 // How (QK^T and PV are dense contractions, so they run on MFMA; bf16 in,
 // fp32 accumulate):
-//  * A wave owns 32 query rows of one query head; the eight waves of a
-//    workgroup share a kv head (two query tiles of the G = 4 heads of a
-//    group, or more tiles of fewer heads).  The workgroup stages each 32-key K / V^T tile once into LDS
+//  * A wave owns 32 query rows of one query head; the four waves of a
+//    workgroup share a kv head (the G = 4 heads of a query tile, or more
+//    tiles of fewer heads).  The workgroup stages each 32-key K / V^T tile once into LDS
 //    (K chunks XOR-swizzled, V^T rows padded, so that the MFMA operand reads
 //    are free of bank conflicts),
 //    double-buffered: the next tile's global loads fly while the current
 //    tile's MFMAs run, one barrier per tile.  Block ids come through the
-//    scalar cache.  Two waves share each SIMD.
+//    scalar cache.  Two workgroups share each CU, so the two waves on a
+//    SIMD belong to different workgroups and do not pass their barriers
+//    together: one's softmax can overlap the other's MFMAs.
 //  * Scores are formed transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 //    (keys are MFMA rows, queries columns): every lane then owns one query
 //    column, and the softmax statistics and the rescaling of O^T stay in the
@@ -51,12 +53,12 @@ __device__ __forceinline__ int kswz(int r) { return swap23(r) & 15; }
 // Sequences of a launch are ordered by work when there are at most this many.
 constexpr int kPrefillSortMax = 256;
 
-// Waves per workgroup: two query tiles of four heads (or more tiles of
+// Waves per workgroup: the four heads of a query tile (or more tiles of
 // fewer heads) share every staged K / V tile.
-constexpr int kPrefillWaves = 8;
+constexpr int kPrefillWaves = 4;
 
 template <int KV, int B, int G>
-__global__ void __launch_bounds__(kPrefillWaves * 64) prefill_kernel(PrefillArgs a, const int32_t* __restrict__ block_table,
+__global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillArgs a, const int32_t* __restrict__ block_table,
                                                         const int32_t* __restrict__ cu_q_lens,
                                                         const int32_t* __restrict__ seq_lens) {
   constexpr int D = 128;
@@ -141,39 +143,51 @@ __global__ void __launch_bounds__(kPrefillWaves * 64) prefill_kernel(PrefillArgs
   const float c = KV == KV_FP8 ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
   const float v_mul = KV == KV_FP8 ? a.v_scale[kvh] : 1.f;
 
-  // ---- staging of one tile by the whole workgroup: each thread moves one
-  // 16-byte chunk of K (row kr, column chunk kcc) and one of V^T (head dim
-  // vd, 8-key group vkc).  Keys past the workgroup's range re-read its last
-  // key (their scores are masked, their V zeroed).
-  static_assert(kPrefillWaves * 64 == KT * 16 && kPrefillWaves * 64 == D * 4, "one chunk of K and V per thread");
+  // ---- staging of one tile by the whole workgroup: each thread moves NCH
+  // 16-byte chunks of K (chunk i: row i / 16, column chunk i % 16) and NCH of
+  // V^T (chunk i: head dim i / 4, 8-key group i % 4), chunks tid and
+  // tid + 64 * kPrefillWaves.
+  constexpr int NCH = KT * 16 / (kPrefillWaves * 64);
+  static_assert(NCH * kPrefillWaves * 64 == KT * 16 && NCH * kPrefillWaves * 64 == D * 4 && NCH <= 2,
+                "whole chunks of K and V per thread");
   static_assert(B == KT || 2 * B == KT, "a tile is one or two blocks");
-  const int kr = tid >> 4, kcc = tid & 15;
-  const int vd = tid >> 2, vkc = tid & 3;
   // Per-thread constants: the chunk's offset inside its block's tile, which
   // of the tile's two blocks holds it (block 16: keys 16..31 and 8-key
   // groups 2, 3), and its LDS address.  A tile past the last key reads the
   // last block again (tile_ids clamps), so every address stays inside an
   // allocated block; those keys are masked.
   constexpr uint64_t kBlockTile = uint64_t(B) * D * ES;    // bytes of one (block, kv head) tile
-  const uint64_t k_lane = uint64_t(((kr % B) * D + kcc * 8) * ES);
-  const uint64_t v_lane = uint64_t((vd * B + (8 * vkc) % B) * ES);
-  const bool k_hi = B != KT && kr >= B;
-  const bool v_hi = B != KT && 8 * vkc >= B;
-  const int k_lds = kr * KROW + (kcc ^ kswz(kr)) * 16;
-  const int v_lds = KBUF + vd * VROW + vkc * 16;
+  auto k_lane = [&](int i) { return uint64_t((((i >> 4) % B) * D + (i & 15) * 8) * ES); };
+  auto v_lane = [&](int i) { return uint64_t(((i >> 2) * B + (8 * (i & 3)) % B) * ES); };
+  auto k_hi = [&](int i) { return B != KT && (i >> 4) >= B; };
+  auto v_hi = [&](int i) { return B != KT && 8 * (i & 3) >= B; };
+  auto k_lds = [&](int i) { return (i >> 4) * KROW + ((i & 15) ^ kswz(i >> 4)) * 16; };
+  auto v_lds = [&](int i) { return KBUF + (i >> 2) * VROW + (i & 3) * 16; };
+  const int ci0 = tid, ci1 = tid + kPrefillWaves * 64;
+  const uint64_t k_lane0 = k_lane(ci0), k_lane1 = k_lane(ci1), v_lane0 = v_lane(ci0), v_lane1 = v_lane(ci1);
+  const bool k_hi0 = k_hi(ci0), k_hi1 = k_hi(ci1), v_hi0 = v_hi(ci0), v_hi1 = v_hi(ci1);
+  const int k_lds0 = k_lds(ci0), k_lds1 = k_lds(ci1), v_lds0 = v_lds(ci0), v_lds1 = v_lds(ci1);
   // (macros over plain variables: two staging sets, kept in registers)
 #define PA_STAGE_LOAD(P, KT_, ID0, ID1)                                                                   \
   do {                                                                                                \
     const uint64_t t0_ = (uint64_t(uint32_t(ID0)) * uint32_t(Hkv) + uint32_t(kvh)) * kBlockTile;       \
     const uint64_t t1_ = (uint64_t(uint32_t(ID1)) * uint32_t(Hkv) + uint32_t(kvh)) * kBlockTile;       \
-    P##k = *reinterpret_cast<const typename Raw::T*>(kpool + (k_hi ? t1_ : t0_) + k_lane);            \
-    P##v = *reinterpret_cast<const typename Raw::T*>(vpool + (v_hi ? t1_ : t0_) + v_lane);            \
+    P##k0 = *reinterpret_cast<const typename Raw::T*>(kpool + (k_hi0 ? t1_ : t0_) + k_lane0);         \
+    P##v0 = *reinterpret_cast<const typename Raw::T*>(vpool + (v_hi0 ? t1_ : t0_) + v_lane0);         \
+    if constexpr (NCH > 1) {                                                                          \
+      P##k1 = *reinterpret_cast<const typename Raw::T*>(kpool + (k_hi1 ? t1_ : t0_) + k_lane1);       \
+      P##v1 = *reinterpret_cast<const typename Raw::T*>(vpool + (v_hi1 ? t1_ : t0_) + v_lane1);       \
+    }                                                                                                 \
   } while (0)
 #define PA_STAGE_STORE(P, BUF)                                                                        \
   do {                                                                                                \
     char* sb_ = smem[BUF];                                                                            \
-    *reinterpret_cast<uint4*>(sb_ + k_lds) = Raw::to_bf16(P##k);                                      \
-    *reinterpret_cast<uint4*>(sb_ + v_lds) = Raw::to_bf16(P##v);                                      \
+    *reinterpret_cast<uint4*>(sb_ + k_lds0) = Raw::to_bf16(P##k0);                                    \
+    *reinterpret_cast<uint4*>(sb_ + v_lds0) = Raw::to_bf16(P##v0);                                    \
+    if constexpr (NCH > 1) {                                                                          \
+      *reinterpret_cast<uint4*>(sb_ + k_lds1) = Raw::to_bf16(P##k1);                                  \
+      *reinterpret_cast<uint4*>(sb_ + v_lds1) = Raw::to_bf16(P##v1);                                  \
+    }                                                                                                 \
   } while (0)
   // block ids of a tile's (at most two) blocks, read through the scalar cache
   auto tile_ids = [&](int kt, int& id0, int& id1) __attribute__((always_inline)) {
@@ -289,7 +303,7 @@ __global__ void __launch_bounds__(kPrefillWaves * 64) prefill_kernel(PrefillArgs
   };
 
   const int last = n_tiles_wg - 1;
-  typename Raw::T sa_k, sa_v, sb_k, sb_v;
+  typename Raw::T sa_k0{}, sa_v0{}, sb_k0{}, sb_v0{}, sa_k1{}, sa_v1{}, sb_k1{}, sb_v1{};
   int j0, j1;
   tile_ids(0, j0, j1);
   PA_STAGE_LOAD(sa_, 0, j0, j1);
