@@ -32,7 +32,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0       # published dense bf16 matrix peak
 # and WRITE_SIZE passes scaled by the same counters on a plain 1 GiB copy
 # (bench.py --copy-probe 1024), and the hash of the kernel sources they were
 # taken on: once those sources change the figure no longer applies.
-DECODE_TRAFFIC = {"sources_sha256": "f29cab83c54e3ac47cc93dc286f7b8c7b6a441f2a19ded7c3c14b0b5f4d40087",
+DECODE_TRAFFIC = {"sources_sha256": "b1fb87545df2124622209ac63ea3c04638974d5d477a6e561275375062b838a6",
                   "bytes_per_launch": 305688693}
 DECODE_SOURCES = ("decode_kernel.h", "pa_device.h", "pa_internal.h", "decode_bf16.hip")
 

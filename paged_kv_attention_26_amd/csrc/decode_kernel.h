@@ -18,9 +18,11 @@
 //  * A (sequence, kv head) whose units all fall in one wave's range is
 //    written out directly.  Otherwise each wave that touched it writes a
 //    partial (max, sum, acc) -- at most two per wave, for the first and the
-//    last item of its range.  After its whole range a wave counts itself in
-//    on those items; the last of an item's waves to arrive merges the
-//    partials by log-sum-exp rescaling, in the same launch.
+//    last item of its range -- and counts itself in on the item: on its
+//    first item as soon as that partial is stored (if its range goes on),
+//    on its last item after the range.  The last of an item's waves to
+//    arrive merges the partials by log-sum-exp rescaling, in the same
+//    launch.
 //  * A scalar cursor walks the steps of the range across items: block ids
 //    are fetched one 64-token step ahead of their use, and every K/V load is
 //    a raw buffer load of one (block, kv head) tile (a descriptor, one lane
@@ -29,7 +31,8 @@
 //    after this step's scores, its V tile right after this step's PV, so a
 //    wave keeps one step of K and V in flight while it computes -- also from
 //    the last step of one item into the first of the next, whose query is
-//    fetched along with them.
+//    fetched along with them.  Past the range's last step the descriptors
+//    are empty: those loads return zeros without touching memory.
 //  * QK^T: a key row is spread over LPR lanes; each lane forms partial dot
 //    products for the G heads with v_dot2_f32_bf16 (fp32 FMA for fp32
 //    caches).  The G partials are reduced by a transpose-reduce inside
