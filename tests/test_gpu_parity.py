@@ -235,7 +235,28 @@ def chunk_batch(name, P, q, B=16, Hq=32, Hkv=8, seed=41, kv="bf16"):
                          prior_lens=P, new_lens=q, is_chunk=np.ones(n, bool), rng=rng)
 
 
+def spiky_batch(name, P, q, spikes=((1 / 3, 8.0), (2 / 3, 3.0), (1.0, 6.0))):
+    """A chunk batch whose keys at a few late positions are scaled up, so that
+    a query column's running maximum jumps well after the first key tile: by
+    more than 2^8 in exp2 units for the larger factors (the attention kernels
+    rescale their accumulators), by less for the smaller one (they keep the
+    stale maximum)."""
+    b = chunk_batch(name, P, q, Hq=8, Hkv=2)
+    off = b.tok_offsets
+    kf = W.bf16_bits_to_f32(b.k).copy()
+    for s in range(b.num_seqs):
+        L = int(b.prior_lens[s] + b.new_lens[s])
+        for frac, f in spikes:
+            pos = min(L - 1, int(frac * L))
+            if pos >= 32:                                 # past the first key tile
+                kf[off[s] + pos] *= f
+    b.k = W.to_bf16_bits(kf)
+    return b
+
+
 CHUNKS = {
+    "spike": lambda: spiky_batch("spike", [300, 1000, 40, 0], [64, 37, 100, 80]),
+    "spike-verify": lambda: spiky_batch("spike-verify", [300, 1000, 4100], [5, 8, 3]),
     "c4s": lambda: W.config4(small=True),
     "prefix0": lambda: chunk_batch("prefix0", [0, 0], [37, 64]),
     "ragged": lambda: chunk_batch("ragged", [5, 100, 33, 512, 0], [1, 31, 33, 97, 129]),
