@@ -73,6 +73,19 @@ def skew_batch():
                          prior_lens=prior, new_lens=new, is_chunk=np.zeros(len(lens), bool), rng=rng)
 
 
+def many_batch():
+    """600 short sequences (0 to 200 tokens): more sequences than threads in a
+    workgroup, so the per-sequence prefixes built in LDS take several
+    sequences per thread."""
+    rng = np.random.default_rng(79)
+    lens = rng.integers(0, 201, 600)
+    lens[::97] = 0
+    prior = np.maximum(lens - 1, 0)
+    new = (lens > 0).astype(np.int64)
+    return W.paged_batch("many-bf16", 79, kv_dtype="bf16", io_dtype="bf16", Hq=8, Hkv=2, d=128, B=16,
+                         prior_lens=prior, new_lens=new, is_chunk=np.zeros(len(lens), bool), rng=rng)
+
+
 SMALL = {
     "c1": lambda: W.config1(),
     "c2s": lambda: W.config2(small=True),
@@ -82,6 +95,7 @@ SMALL = {
     "edge32": lambda: edge_batch("bf16", 32),
     "edge-f32": lambda: edge_batch("f32", 16),
     "skew": skew_batch,
+    "many": many_batch,
 }
 
 
@@ -339,7 +353,7 @@ def test_prefill_full_mixed_batch_sampled():
 
 
 # ------------------------------------------------ pack (KV hand-off)
-@pytest.mark.parametrize("name", ["c1", "c2s", "c3s32", "edge16", "skew"])
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s32", "edge16", "skew", "many"])
 def test_pack_is_bit_exact(name):
     from oracle import paged
     from paged_kv_attention_26_amd import runner
