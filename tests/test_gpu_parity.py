@@ -268,7 +268,18 @@ def spiky_batch(name, P, q, spikes=((1 / 3, 8.0), (2 / 3, 3.0), (1.0, 6.0))):
     return b
 
 
+def many_chunks():
+    """300 chunk sequences: more than the prefill kernel ranks by work in
+    LDS, so they run in launch order."""
+    rng = np.random.default_rng(80)
+    P = rng.integers(0, 120, 300)
+    q = rng.integers(1, 41, 300)
+    return W.paged_batch("many-chunks", 80, kv_dtype="bf16", io_dtype="bf16", Hq=8, Hkv=2, d=128, B=16,
+                         prior_lens=P, new_lens=q, is_chunk=np.ones(300, bool), rng=rng)
+
+
 CHUNKS = {
+    "many": many_chunks,
     "spike": lambda: spiky_batch("spike", [300, 1000, 40, 0], [64, 37, 100, 80]),
     "spike-verify": lambda: spiky_batch("spike-verify", [300, 1000, 4100], [5, 8, 3]),
     "c4s": lambda: W.config4(small=True),
