@@ -150,7 +150,8 @@ def extras(pa, runner, W, torch, groups=EXTRA_GROUPS):
         rows = int(np.sum(b.total_lens))
         k = torch.empty((rows, b.num_kv_heads, b.head_dim), dtype=torch.bfloat16, device="cuda")
         v = torch.empty_like(k)
-        med_p, _, _ = timed_calls(lambda: runner.pack_all(g, k_out=k, v_out=v), 20)
+        pargs = runner.pack_args(g)                          # uploaded once: the timed call is pa_pack_kv alone
+        med_p, _, _ = timed_calls(lambda: runner.pack_all(g, k_out=k, v_out=v, args=pargs), 20)
         d = copy.copy(b)
         d.free_order = np.random.default_rng(2002).permutation(b.num_blocks)
         gd = runner.prepare(d, fill=False)

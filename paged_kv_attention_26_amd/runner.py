@@ -114,13 +114,19 @@ def decode_step(g: GpuBatch, out=None, partition_tokens=0, workspace=None) -> to
                      partition_tokens=partition_tokens, workspace=workspace)
 
 
-def pack_all(g: GpuBatch, device="cuda", k_out=None, v_out=None):
-    """pa_pack_kv of every sequence's tokens (cached and stepped), in order."""
+def pack_args(g: GpuBatch, device="cuda") -> dict:
+    """Device arguments of pa_pack_kv for every sequence's tokens (cached and
+    stepped), in order."""
     lens = np.asarray(g.batch.total_lens, dtype=np.int64)
     cu = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
-    table = _t(_table_rows(g.tables, g.pad), device)
-    return pa.pack_kv(g.cache, table, _t(lens.astype(np.int32), device), _t(cu, device), int(lens.max(initial=0)),
-                      int(lens.sum()), k_out=k_out, v_out=v_out)
+    return dict(table=_t(_table_rows(g.tables, g.pad), device), lens=_t(lens.astype(np.int32), device),
+                cu=_t(cu, device), max_len=int(lens.max(initial=0)), rows=int(lens.sum()))
+
+
+def pack_all(g: GpuBatch, device="cuda", k_out=None, v_out=None, args=None):
+    """pa_pack_kv of every sequence's tokens (cached and stepped), in order."""
+    p = args if args is not None else pack_args(g, device)
+    return pa.pack_kv(g.cache, p["table"], p["lens"], p["cu"], p["max_len"], p["rows"], k_out=k_out, v_out=v_out)
 
 
 def all_slots(g: GpuBatch, device="cuda") -> torch.Tensor:
