@@ -81,7 +81,7 @@ typedef struct {
   int32_t dtype; /* pa_dtype */
 } pa_kv_cache;
 
-/* Store new K/V rows into their slots (nanoPD page, "paged KV store" of the
+/* Store new K/V rows into their slots (nanoPD page, the paged-KV store of the
  * paged_attention extension; serving-stack page section 2.3: a token goes to
  * its sequence's last block at offset length % block_size).
  *
@@ -101,9 +101,9 @@ typedef struct {
 int pa_store_kv(const pa_kv_cache* cache, const void* k_new, const void* v_new, int32_t in_dtype,
                 const int32_t* slot_mapping, int32_t num_tokens, void* hip_stream);
 
-/* Copy whole blocks (copy on write for forked / beam sequences: nanoPD page
- * "写时复制(Copy-on-Write)用于束搜索和投机解码的分支"; serving-stack page
- * section 2.3, cow()).
+/* Copy whole blocks (copy on write for forked / beam sequences: nanoPD page,
+ * section 分页KV缓存, where copy on write serves beam search and
+ * speculative-decoding branches; serving-stack page section 2.3, cow()).
  *   src_dst : [num_pairs][2] int32 pairs (src, dst); for each pair
  *             k_cache[dst] = k_cache[src] and v_cache[dst] = v_cache[src]
  *             (all kv heads, the whole block, bit-exact).

@@ -1,10 +1,10 @@
 // Paged KV store (scatter of new K/V rows into their slots) and whole-block
 // copy for copy-on-write, gfx950.
 //
-// Store: the nanoPD page names a "paged KV store op" beside its attention
-// kernel; the serving-stack page, section 2.3, places a sequence's new token
-// at offset length % block_size of its last block.  Here a slot is
-// physical_block * block_size + offset.
+// Store: the nanoPD page lists a store operation for the paged KV cache
+// beside its attention kernel; the serving-stack page, section 2.3, places a
+// sequence's new token at offset length % block_size of its last block.
+// Here a slot is physical_block * block_size + offset.
 // Pack: the inverse gather, a request's cached K/V out of its blocks into
 // contiguous token rows, the form in which the prefill side hands KV to the
 // decode side (nanoPD page, 异步KV传输; PD-engineering page section 3).
