@@ -40,15 +40,44 @@ __global__ void __launch_bounds__(256) store_kv_kernel(StoreArgs a) {
     vsc = a.v_scale[h];
   }
 
+  // Every load of a thread goes out before its first store (the stores could
+  // alias the inputs as far as the compiler knows, so a load-store loop would
+  // keep one load in flight per thread).  Loads are unconditional, clamped to
+  // the workgroup's last token; only the stores are guarded.
+  const int nt = min(64, a.num_tokens - t0);
+  const int nkc = nt * cpr;                                // key chunks of the workgroup
+  constexpr int KI = (64 * 128 / EPC) / 256;               // key chunks per thread at head_dim 128
+  uint4 kx[KI];
+  int ks[KI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int idx = min(int(threadIdx.x) + 256 * i, nkc - 1);
+    kx[i] = *reinterpret_cast<const uint4*>(kin + ((size_t(t0 + idx / cpr) * H + h) * D + size_t(idx % cpr) * EPC) * IN_ES);
+    ks[i] = a.slot_mapping[t0 + idx / cpr];
+  }
+  // values: lane = token, wave w takes chunks w, w + 4, ...
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int tv = t0 + min(lane, nt - 1);
+  constexpr int VI = (128 / EPC) / 4;                      // value chunks per lane at head_dim 128
+  const int vslot = a.slot_mapping[tv];
+  uint4 vx[VI];
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int c = min(wave + 4 * i, cpr - 1);
+    vx[i] = *reinterpret_cast<const uint4*>(vin + ((size_t(tv) * H + h) * D + size_t(c) * EPC) * IN_ES);
+  }
+
   // ---- keys: contiguous rows
-  for (int idx = threadIdx.x; idx < 64 * cpr; idx += 256) {
-    const int t = t0 + idx / cpr;
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int idx = threadIdx.x + 256 * i;
+    if (idx >= nkc) break;
     const int c = idx % cpr;
-    if (t >= a.num_tokens) continue;
-    const int slot = a.slot_mapping[t];
+    const int slot = ks[i];
     if (slot < 0) continue;
     const int blk = slot / BS, off = slot % BS;
-    const uint4 x = *reinterpret_cast<const uint4*>(kin + ((size_t(t) * H + h) * D + size_t(c) * EPC) * IN_ES);
+    const uint4 x = kx[i];
     char* dst = kc + ((size_t(blk) * H + h) * BS + off) * size_t(D) * OUT_ES + size_t(c) * EPC * OUT_ES;
     if constexpr (KV != KV_FP8) {
       *reinterpret_cast<uint4*>(dst) = x;
@@ -67,16 +96,16 @@ __global__ void __launch_bounds__(256) store_kv_kernel(StoreArgs a) {
   }
 
   // ---- values: transposed rows, lane = token
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int t = t0 + lane;
-  int slot = -1;
-  if (t < a.num_tokens) slot = a.slot_mapping[t];
+  if (lane >= nt) return;
+  const int slot = vslot;
   if (slot < 0) return;
   const int blk = slot / BS, off = slot % BS;
   char* vrow = vc + ((size_t(blk) * H + h) * D) * size_t(BS) * OUT_ES + size_t(off) * OUT_ES;
-  for (int c = wave; c < cpr; c += 4) {
-    const uint4 x = *reinterpret_cast<const uint4*>(vin + ((size_t(t) * H + h) * D + size_t(c) * EPC) * IN_ES);
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int c = wave + 4 * i;
+    if (c >= cpr) break;
+    const uint4 x = vx[i];
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
     const int d0 = c * EPC;
     if constexpr (KV == KV_F32) {
