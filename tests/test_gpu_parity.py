@@ -505,3 +505,90 @@ def test_prefix_cache_conversations(kv, small):
     assert held == [b for b in range(w.num_blocks) if bm.ref_count(b)]
     assert np.array_equal(bits(cache.k_cache, kv)[held], oracle_bits(kc, kv)[held])
     assert np.array_equal(bits(cache.v_cache, kv)[held], oracle_bits(vc, kv)[held])
+
+
+# ------------------------------------------------ seeded random shapes
+def random_decode_batch(seed):
+    """A seeded random decode batch: batch size, length mix (empty, single
+    token, block edges, long), group size, block size, head dim, cache dtype
+    and split grain all drawn from the supported set."""
+    rng = np.random.default_rng(9000 + seed)
+    kv = ["bf16", "fp8", "f32"][seed % 3]
+    d = 64 if kv == "f32" else int(rng.choice([64, 128]))
+    if kv == "fp8":
+        d = 128
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    B = int(rng.choice([16, 32]))
+    S = int(rng.integers(1, 90))
+    kinds = rng.integers(0, 5, S)
+    lens = np.where(kinds == 0, 0, np.where(kinds == 1, rng.integers(1, 3, S),
+                    np.where(kinds == 2, B * rng.integers(1, 8, S) + rng.integers(-1, 2, S),
+                             rng.integers(1, 3000, S))))
+    lens = np.maximum(lens, 0)
+    prior = np.maximum(lens - 1, 0)
+    new = (lens > 0).astype(np.int64)
+    io = "f32" if kv == "f32" else "bf16"
+    b = W.paged_batch(f"rand-dec-{seed}", 9000 + seed, kv_dtype=kv, io_dtype=io, Hq=G * Hkv, Hkv=Hkv, d=d, B=B,
+                      prior_lens=prior, new_lens=new, is_chunk=np.zeros(S, bool), rng=rng)
+    return b, int(rng.choice([0, 64, 128, 256, 512]))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_random_shapes(seed):
+    from paged_kv_attention_26_amd import runner
+    batch, part = random_decode_batch(seed)
+    say(f"[gpu] random decode {batch.name}: S={batch.num_seqs} {batch.kv_dtype} d={batch.head_dim} "
+        f"G={batch.num_q_heads // batch.num_kv_heads} Hkv={batch.num_kv_heads} B={batch.block_size} part={part}")
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    out = out_f64(runner.decode_step(g, partition_tokens=part))
+    torch.cuda.synchronize()
+    st = OS.build(batch)
+    ref = OS.decode_ref(batch, st)
+    assert np.all(np.isfinite(out))
+    err = np.max(np.abs(out - ref)) if out.size else 0.0
+    say(f"      max abs err {err:.3e}")
+    assert err < TOL[batch.kv_dtype]
+
+
+def random_chunk_batch(seed):
+    """A seeded random chunked-prefill batch (chunks of 1 to 300 tokens on
+    prefixes of 0 to 2000, some sequences decoding beside them); every fourth
+    seed keeps chunks within 32 / G tokens, the speculative-verification form."""
+    rng = np.random.default_rng(9500 + seed)
+    kv = ["bf16", "fp8"][seed % 2]
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    B = int(rng.choice([16, 32]))
+    S = int(rng.integers(1, 24))
+    is_chunk = rng.random(S) < 0.7
+    is_chunk[0] = True
+    P = rng.integers(0, 2000, S)
+    qmax = max(2, 32 // G + 1) if seed % 4 == 3 else 300
+    q = np.where(is_chunk, rng.integers(1, qmax, S), 1)
+    return W.paged_batch(f"rand-chunk-{seed}", 9500 + seed, kv_dtype=kv, io_dtype="bf16", Hq=G * Hkv, Hkv=Hkv,
+                         d=128, B=B, prior_lens=P, new_lens=q, is_chunk=is_chunk, rng=rng)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_prefill_random_shapes(seed):
+    from paged_kv_attention_26_amd import runner
+    batch = random_chunk_batch(seed)
+    say(f"[gpu] random prefill {batch.name}: S={batch.num_seqs} {batch.kv_dtype} "
+        f"G={batch.num_q_heads // batch.num_kv_heads} Hkv={batch.num_kv_heads} B={batch.block_size}")
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    out = out_f64(runner.chunk_step(g))
+    torch.cuda.synchronize()
+    st = OS.build(batch)
+    ref = OS.chunk_ref(batch, st)
+    assert np.all(np.isfinite(out))
+    err = np.max(np.abs(out - ref))
+    say(f"      max abs err {err:.3e}")
+    assert err < TOL[batch.kv_dtype]
+    if (~batch.is_chunk).any():
+        dref = OS.decode_ref(batch, st)
+        derr = np.max(np.abs(out_f64(runner.decode_step(g)) - dref))
+        say(f"      decode max abs err {derr:.3e}")
+        assert derr < TOL[batch.kv_dtype]
