@@ -18,13 +18,24 @@ namespace pa {
 // One workgroup = 64 consecutive tokens x one kv head.
 //  K: 16-byte input chunks, mapped so that consecutive lanes cover one key
 //     row: reads and writes are both contiguous.
-//  V: lane = token, so that tokens landing at consecutive offsets of one
-//     block write neighbouring elements of each transposed head-dim row.
+//  V: read with lane = token.  Tokens that land at consecutive offsets of one
+//     block form a run; the first RMAX runs of the workgroup are placed in
+//     an LDS tile [head dim][run, offset in block] of cache elements and
+//     leave in 16-byte pieces of transposed block rows (one store per piece
+//     a run covers whole; element stores for the pieces at its ends), so the
+//     lanes of a wave cover whole block rows one after another.  Tokens of
+//     later runs (a workgroup of scattered single tokens) are written
+//     element by element straight from registers.
 template <int KV>
 __global__ void __launch_bounds__(256) store_kv_kernel(StoreArgs a) {
   constexpr int IN_ES = (KV == KV_F32) ? 4 : (KV == KV_FP8_RAW ? 1 : 2);   // input element bytes
   constexpr int OUT_ES = (KV == KV_F32) ? 4 : (KV == KV_BF16 ? 2 : 1);
   constexpr int EPC = 16 / IN_ES;                          // elements per 16-byte chunk
+  constexpr int TPG = 16 / OUT_ES;                         // tokens per 16-byte piece of a block row
+  constexpr int COLS = OUT_ES == 4 ? 64 : 128;             // LDS columns: RMAX runs x block size
+  constexpr int ROWB = COLS * OUT_ES + 16;                 // LDS bytes per head-dim row (padded)
+  __shared__ __attribute__((aligned(16))) char s_vt[128 * ROWB];
+  __shared__ int s_rblk[64], s_rlo[64], s_rhi[64];        // per staged run: block, offsets [lo, hi)
   const int h = blockIdx.y;
   const int t0 = blockIdx.x * 64;
   const int cpr = a.head_dim / EPC;                        // chunks per row
@@ -95,37 +106,103 @@ __global__ void __launch_bounds__(256) store_kv_kernel(StoreArgs a) {
     }
   }
 
-  // ---- values: transposed rows, lane = token
-  if (lane >= nt) return;
-  const int slot = vslot;
-  if (slot < 0) return;
-  const int blk = slot / BS, off = slot % BS;
-  char* vrow = vc + ((size_t(blk) * H + h) * D) * size_t(BS) * OUT_ES + size_t(off) * OUT_ES;
+  // ---- runs of the values' slots (every wave derives them from the slots
+  // it loaded; wave 0 records each staged run's block and offsets)
+  const int BS_ = BS;
+  const int RMAX = COLS / BS_;
+  const int slot = lane < nt ? vslot : -1;
+  int prev = __shfl(slot, (lane + 63) & 63);
+  if (lane == 0) prev = -1;
+  const bool live = slot >= 0;
+  const int off = live ? slot % BS_ : 0;
+  const bool starts = live && (prev < 0 || slot != prev + 1 || off == 0);
+  const uint64_t sb = __ballot(starts);
+  const uint64_t lb = __ballot(live);
+  const int r = __popcll(sb & ((2ull << lane) - 1ull)) - 1;  // run index of this token
+  const bool staged = live && r < RMAX;
+  const int nrun = min(__popcll(sb), RMAX);
+  if (wave == 0 && staged) {
+    const bool ends = lane == 63 || !((lb >> (lane + 1)) & 1ull) || ((sb >> (lane + 1)) & 1ull);
+    if (starts) {
+      s_rblk[r] = slot / BS_;
+      s_rlo[r] = off;
+    }
+    if (ends) s_rhi[r] = off + 1;
+  }
+
+  // ---- values into LDS, encoded: s_vt[d * ROWB + (r * BS + off) * OUT_ES];
+  // tokens of runs past the staged ones go out element by element
+  char* col = s_vt + (staged ? r * BS_ + off : 0) * OUT_ES;
+  char* vrow = vc + ((size_t(live ? slot / BS_ : 0) * H + h) * D) * size_t(BS_) * OUT_ES + size_t(off) * OUT_ES;
 #pragma unroll
   for (int i = 0; i < VI; ++i) {
     const int c = wave + 4 * i;
     if (c >= cpr) break;
     const uint4 x = vx[i];
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-    const int d0 = c * EPC;
+    uint8_t e8[16];
+    uint32_t e32[4];
+    uint16_t e16[8];
     if constexpr (KV == KV_F32) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        *reinterpret_cast<uint32_t*>(vrow + size_t(d0 + e) * BS * 4) = w[e];
+      for (int e = 0; e < 4; ++e) e32[e] = w[e];
     } else if constexpr (KV == KV_BF16) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<uint16_t*>(vrow + size_t(d0 + 2 * e) * BS * 2) = uint16_t(w[e] & 0xFFFFu);
-        *reinterpret_cast<uint16_t*>(vrow + size_t(d0 + 2 * e + 1) * BS * 2) = uint16_t(w[e] >> 16);
+        e16[2 * e] = uint16_t(w[e] & 0xFFFFu);
+        e16[2 * e + 1] = uint16_t(w[e] >> 16);
       }
     } else if constexpr (KV == KV_FP8_RAW) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) *reinterpret_cast<uint8_t*>(vrow + size_t(d0 + e) * BS) = uint8_t(w[e >> 2] >> (8 * (e & 3)));
+      for (int e = 0; e < 16; ++e) e8[e] = uint8_t(w[e >> 2] >> (8 * (e & 3)));
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<uint8_t*>(vrow + size_t(d0 + 2 * e) * BS) = uint8_t(e4m3_encode(bf16_lo(w[e]) / vsc));
-        *reinterpret_cast<uint8_t*>(vrow + size_t(d0 + 2 * e + 1) * BS) = uint8_t(e4m3_encode(bf16_hi(w[e]) / vsc));
+        e8[2 * e] = uint8_t(e4m3_encode(bf16_lo(w[e]) / vsc));
+        e8[2 * e + 1] = uint8_t(e4m3_encode(bf16_hi(w[e]) / vsc));
+      }
+    }
+    const int d0 = c * EPC;
+    if (staged) {
+      char* p = col + size_t(d0) * ROWB;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        if constexpr (OUT_ES == 4) *reinterpret_cast<uint32_t*>(p + e * ROWB) = e32[e];
+        else if constexpr (OUT_ES == 2) *reinterpret_cast<uint16_t*>(p + e * ROWB) = e16[e];
+        else p[e * ROWB] = char(e8[e]);
+      }
+    } else if (live) {
+      char* q = vrow + size_t(d0) * BS_ * OUT_ES;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        if constexpr (OUT_ES == 4) *reinterpret_cast<uint32_t*>(q + e * BS_ * 4) = e32[e];
+        else if constexpr (OUT_ES == 2) *reinterpret_cast<uint16_t*>(q + e * BS_ * 2) = e16[e];
+        else q[e * BS_] = char(e8[e]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- staged runs out: item = (run, head-dim row, 16-byte piece of the
+  // block row); consecutive items walk the pieces of a row, then the rows
+  const int ppr = BS_ / TPG;                               // pieces per block row
+  const int items = nrun * ppr * D;
+  for (int it = threadIdx.x; it < items; it += 256) {
+    const int k = it % ppr;
+    const int d = (it / ppr) % D;
+    const int rr = it / (ppr * D);
+    const int lo = s_rlo[rr], hi = s_rhi[rr];
+    const int c0 = k * TPG, c1 = c0 + TPG;
+    if (hi <= c0 || c1 <= lo) continue;                    // piece outside the run
+    const char* src = s_vt + d * ROWB + rr * BS_ * OUT_ES;
+    char* dst = vc + ((size_t(s_rblk[rr]) * H + h) * D + d) * size_t(BS_) * OUT_ES;
+    if (lo <= c0 && c1 <= hi) {
+      *reinterpret_cast<uint4*>(dst + c0 * OUT_ES) = *reinterpret_cast<const uint4*>(src + c0 * OUT_ES);
+    } else {
+      for (int o = max(lo, c0); o < min(hi, c1); ++o) {
+        if constexpr (OUT_ES == 4) *reinterpret_cast<uint32_t*>(dst + 4 * o) = *reinterpret_cast<const uint32_t*>(src + 4 * o);
+        else if constexpr (OUT_ES == 2) *reinterpret_cast<uint16_t*>(dst + 2 * o) = *reinterpret_cast<const uint16_t*>(src + 2 * o);
+        else dst[o] = src[o];
       }
     }
   }

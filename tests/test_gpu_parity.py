@@ -113,6 +113,63 @@ def test_store_is_bit_exact_over_the_whole_pool(name):
     assert np.array_equal(bits(g.cache.v_cache, batch.kv_dtype), oracle_bits(st.vc, batch.kv_dtype))
 
 
+def slot_pattern(rng, num_blocks, B, T):
+    """T distinct slots (or -1) mixing whole blocks, runs that start at odd
+    offsets and cross block ends, short aligned runs, skipped tokens inside
+    runs and lone tokens, over a random block order."""
+    blocks = list(rng.permutation(num_blocks))
+    out = []
+    while len(out) < T and len(blocks) >= 2:
+        kind = int(rng.integers(0, 5))
+        b0, b1 = int(blocks.pop()), int(blocks.pop())
+        if kind == 0:                                       # two whole blocks, in order
+            run = list(range(b0 * B, b0 * B + B)) + list(range(b1 * B, b1 * B + B))
+        elif kind == 1:                                     # odd start, crossing into the next block
+            o = int(rng.integers(1, B))
+            run = list(range(b0 * B + o, b0 * B + B)) + list(range(b1 * B, b1 * B + int(rng.integers(1, B))))
+        elif kind == 2:                                     # aligned but short runs
+            run = list(range(b0 * B, b0 * B + int(rng.integers(1, 8)))) + list(range(b1 * B + 8, b1 * B + 13))
+        elif kind == 3:                                     # a whole block with skipped tokens
+            run = [sl if rng.random() > 0.2 else -1 for sl in range(b0 * B, b0 * B + B)]
+        else:                                               # lone tokens at random offsets
+            run = [b0 * B + int(rng.integers(0, B)), b1 * B + int(rng.integers(0, B)), -1]
+        out.extend(run)
+    return np.asarray(out[:T], dtype=np.int32)
+
+
+@pytest.mark.parametrize("kv,B,D", [("bf16", 16, 128), ("bf16", 32, 64), ("f32", 16, 64), ("f32", 32, 128),
+                                    ("fp8", 16, 128), ("fp8", 32, 128)])
+def test_store_slot_patterns_bit_exact(kv, B, D):
+    """pa_store_kv with arbitrary slot patterns (whole and partial blocks,
+    misaligned and skipped tokens) against the oracle's scatter, bit for bit
+    over the whole poisoned pool."""
+    from oracle import paged
+    from paged_kv_attention_26_amd import binding as pa
+    rng = np.random.default_rng(4242 + B + D)
+    NB, H, T = 96, 2, 700
+    slots = slot_pattern(rng, NB, B, T)
+    T = len(slots)
+    say(f"[gpu] store slot patterns {kv} B{B} d{D}: {T} tokens, {int((slots < 0).sum())} skipped")
+    x = rng.standard_normal((2, T, H, D)).astype(np.float32)
+    scale = (rng.random(H).astype(np.float32) * 0.5 + 0.25) if kv == "fp8" else None
+    if kv == "f32":
+        kin, vin = x[0], x[1]
+        kt, vt = torch.from_numpy(kin).cuda(), torch.from_numpy(vin).cuda()
+        in_dt = "f32"
+    else:
+        kin, vin = W.to_bf16_bits(x[0]), W.to_bf16_bits(x[1])
+        kt = torch.from_numpy(kin.view(np.int16)).view(torch.bfloat16).cuda()
+        vt = torch.from_numpy(vin.view(np.int16)).view(torch.bfloat16).cuda()
+        in_dt = "bf16"
+    cache = pa.alloc_cache(NB, H, B, D, kv, k_scale=scale, v_scale=scale)
+    pa.store_kv(cache, kt, vt, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    kc, vc = paged.new_pools(NB, H, B, D, kv)
+    paged.store_kv(kc, vc, kv, kin, vin, in_dt, slots, k_scale=scale, v_scale=scale)
+    assert np.array_equal(bits(cache.k_cache, kv), oracle_bits(kc, kv))
+    assert np.array_equal(bits(cache.v_cache, kv), oracle_bits(vc, kv))
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 @pytest.mark.parametrize("part", [0, 64, 128, 512])
 def test_decode_matches_oracle(name, part):
