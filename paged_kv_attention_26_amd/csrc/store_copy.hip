@@ -36,10 +36,20 @@ __global__ void __launch_bounds__(256) store_kv_kernel(StoreArgs a) {
   constexpr int ROWB = COLS * OUT_ES + 16;                 // LDS bytes per head-dim row (padded)
   __shared__ __attribute__((aligned(16))) char s_vt[128 * ROWB];
   __shared__ int s_rblk[64], s_rlo[64], s_rhi[64];        // per staged run: block, offsets [lo, hi)
-  const int h = blockIdx.y;
-  const int t0 = blockIdx.x * 64;
-  const int cpr = a.head_dim / EPC;                        // chunks per row
   const int H = a.num_kv_heads, D = a.head_dim, BS = a.block_size;
+  // Workgroup -> (64-token tile, kv head), XCD-aware: workgroup i runs on XCD
+  // i mod 8, and each XCD takes a contiguous stretch of tiles (all heads of a
+  // tile, then the next tile), so that the two workgroups sharing a block that
+  // a run straddles usually meet in one L2 and the block's lines go to memory
+  // whole, and an XCD reads whole input rows.
+  const int ntiles = (a.num_tokens + 63) / 64;
+  const int per_xcd = int(gridDim.x) / 8;
+  const int idx = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
+  if (idx >= ntiles * H) return;                           // padding workgroup, before any barrier
+  const int tile = idx / H;
+  const int h = idx - tile * H;
+  const int t0 = tile * 64;
+  const int cpr = a.head_dim / EPC;                        // chunks per row
 
   const char* kin = static_cast<const char*>(a.k_new);
   const char* vin = static_cast<const char*>(a.v_new);
@@ -348,7 +358,9 @@ hipError_t launch_pack_kv(const PackArgs& a, int es, int num_seqs, int max_block
 
 hipError_t launch_store_kv(const StoreArgs& a, int kv, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
-  dim3 grid((a.num_tokens + 63) / 64, a.num_kv_heads);
+  const int64_t work = int64_t((a.num_tokens + 63) / 64) * a.num_kv_heads;
+  if (work > 0x7FFFFFF0ll) return hipErrorInvalidValue;
+  dim3 grid(uint32_t((work + 7) / 8 * 8));
   switch (kv) {
     case KV_F32: hipLaunchKernelGGL(store_kv_kernel<KV_F32>, grid, dim3(256), 0, s, a); break;
     case KV_BF16: hipLaunchKernelGGL(store_kv_kernel<KV_BF16>, grid, dim3(256), 0, s, a); break;
