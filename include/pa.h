@@ -176,6 +176,18 @@ int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* ou
               int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
               int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Timing hook for measurement (no counterpart in the pages): the next
+ * pa_decode call made on this thread records start_event and stop_event
+ * (hipEvent_t, created by the caller with timing enabled, either may be
+ * NULL) with its kernel's own start and end timestamps, through
+ * hipExtLaunchKernel, instead of marker packets placed around the call in the
+ * stream, which add several microseconds of their own to the window and to
+ * the stream.  One call arms one pa_decode call: that call disarms it at
+ * entry, whether it then launches or not (a call rejected by its checks, or
+ * one with num_seqs == 0, leaves the events untouched).  Passing NULL, NULL
+ * disarms.  Returns PA_OK. */
+int pa_decode_time_next(void* start_event, void* stop_event);
+
 /* Chunked-prefill attention (nanoPD page "分块预填充"; PD-engineering page
  * section 6.1; serving-stack page section 5.2): sequence j appends a chunk
  * of q_len_j = cu_q_lens[j+1] - cu_q_lens[j] tokens, already stored in the

@@ -179,6 +179,21 @@ def decode(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor, context_l
     return out
 
 
+def time_next_decode(start: Optional[torch.cuda.Event], stop: Optional[torch.cuda.Event]) -> None:
+    """Arm pa_decode_time_next: the next decode() on this thread records the
+    two events with its kernel's own start and end timestamps.  The events
+    must exist already (torch creates one at its first record())."""
+    ptrs = []
+    for e in (start, stop):
+        if e is None:
+            ptrs.append(None)
+            continue
+        if not isinstance(e, torch.cuda.Event) or not e.cuda_event:
+            raise ValueError("pass torch.cuda.Event objects that have been recorded once (so that they exist)")
+        ptrs.append(C.c_void_p(e.cuda_event))
+    L.check(L.lib().pa_decode_time_next(ptrs[0], ptrs[1]), "pa_decode_time_next")
+
+
 def prefill_chunk(cache: KVCache, q: torch.Tensor, cu_q_lens: torch.Tensor, seq_lens: torch.Tensor,
                   block_table: torch.Tensor, max_q_len: int, max_seq_len: int, scale: float,
                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

@@ -10,14 +10,16 @@
 #include "pa_internal.h"
 
 namespace pa {
-hipError_t launch_decode_f32(const DecodeArgs&, int, int, int, int64_t, hipStream_t);
-hipError_t launch_decode_bf16(const DecodeArgs&, int, int, int, int64_t, hipStream_t);
-hipError_t launch_decode_fp8(const DecodeArgs&, int, int, int, int64_t, hipStream_t);
+hipError_t launch_decode_f32(const DecodeArgs&, int, int, int, int64_t, hipStream_t, const LaunchEvents&);
+hipError_t launch_decode_bf16(const DecodeArgs&, int, int, int, int64_t, hipStream_t, const LaunchEvents&);
+hipError_t launch_decode_fp8(const DecodeArgs&, int, int, int, int64_t, hipStream_t, const LaunchEvents&);
 }  // namespace pa
 
 namespace {
 
 thread_local char g_err[512] = "";
+// events armed by pa_decode_time_next for this thread's next pa_decode call
+thread_local pa::LaunchEvents g_decode_events;
 
 template <typename... A>
 int fail(int code, const char* fmt, A... args) {
@@ -91,11 +93,12 @@ DecodeWorkspace decode_workspace_layout(int64_t D) {
   return w;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int kv, int D, int B, int G, int64_t upper, hipStream_t s) {
+hipError_t launch_decode(const DecodeArgs& a, int kv, int D, int B, int G, int64_t upper, hipStream_t s,
+                         const LaunchEvents& ev) {
   switch (kv) {
-    case KV_F32: return launch_decode_f32(a, D, B, G, upper, s);
-    case KV_BF16: return launch_decode_bf16(a, D, B, G, upper, s);
-    default: return launch_decode_fp8(a, D, B, G, upper, s);
+    case KV_F32: return launch_decode_f32(a, D, B, G, upper, s, ev);
+    case KV_BF16: return launch_decode_bf16(a, D, B, G, upper, s, ev);
+    default: return launch_decode_fp8(a, D, B, G, upper, s, ev);
   }
 }
 
@@ -179,6 +182,8 @@ int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* ou
               int32_t num_seqs, int32_t num_q_heads, float scale, const int32_t* block_table,
               int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
               int32_t partition_tokens, void* workspace, size_t workspace_bytes_given, void* hip_stream) {
+  const pa::LaunchEvents ev = g_decode_events;             // armed for this call only
+  g_decode_events = pa::LaunchEvents{};
   int rc = check_cache(cache);
   if (rc) return rc;
   if (num_seqs < 0 || num_seqs > kMaxSeqs) return fail(PA_ERR_SHAPE, "num_seqs %d outside 0..%d", num_seqs, kMaxSeqs);
@@ -228,9 +233,15 @@ int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* ou
   const int64_t max_parts = max_context_len > 0 ? (int64_t(max_context_len) + P - 1) / P : 1;
   const int64_t upper_units = int64_t(num_seqs) * cache->num_kv_heads * max_parts;
   hipError_t e = pa::launch_decode(a, kv, cache->head_dim, cache->block_size, G, upper_units,
-                                   static_cast<hipStream_t>(hip_stream));
+                                   static_cast<hipStream_t>(hip_stream), ev);
   if (e == hipErrorInvalidValue) return fail(PA_ERR_UNSUPPORTED, "no decode kernel for this shape");
   if (e != hipSuccess) return hip_fail(e, "pa_decode launch");
+  g_err[0] = 0;
+  return PA_OK;
+}
+
+int pa_decode_time_next(void* start_event, void* stop_event) {
+  g_decode_events = pa::LaunchEvents{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
   g_err[0] = 0;
   return PA_OK;
 }

@@ -5,8 +5,8 @@
 namespace pa {
 
 hipError_t launch_decode_f32(const DecodeArgs& a, int head_dim, int block_size, int group, int64_t upper_items,
-                               hipStream_t s) {
-  return launch_decode_kv<KV_F32>(a, head_dim, block_size, group, upper_items, s);
+                             hipStream_t s, const LaunchEvents& ev) {
+  return launch_decode_kv<KV_F32>(a, head_dim, block_size, group, upper_items, s, ev);
 }
 
 }  // namespace pa

@@ -51,6 +51,8 @@
 
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -714,8 +716,16 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
   }
 }
 
+// A launch whose events take the kernel's own start and end timestamps.
+template <typename K, typename... Args>
+hipError_t launch_with_events(K kern, dim3 grid, dim3 block, size_t lds, hipStream_t s, const LaunchEvents& ev,
+                              Args... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, argv, lds, s, ev.start, ev.stop, 0);
+}
+
 template <int KV, int D, int B, int G>
-hipError_t launch_decode_t(const DecodeArgs& a0, int64_t upper_units, hipStream_t s) {
+hipError_t launch_decode_t(const DecodeArgs& a0, int64_t upper_units, hipStream_t s, const LaunchEvents& ev) {
   auto kern = decode_kernel<KV, D, B, G>;
   const size_t lds = size_t(a0.num_seqs + 1) * sizeof(int);
   static int cached_occ = -1;
@@ -739,15 +749,18 @@ hipError_t launch_decode_t(const DecodeArgs& a0, int64_t upper_units, hipStream_
   if (wgs < 1) wgs = 1;
   DecodeArgs a = a0;
   a.total_waves = int32_t(wgs * 4);
+  if (ev.start || ev.stop)
+    return launch_with_events(kern, dim3(uint32_t(wgs)), dim3(256), lds, s, ev, a, a.block_table, a.context_lens);
   hipLaunchKernelGGL(kern, dim3(uint32_t(wgs)), dim3(256), lds, s, a, a.block_table, a.context_lens);
   return hipGetLastError();
 }
 
 // Dispatch over the compiled (head_dim, block_size, group) set for one cache dtype.
 template <int KV>
-hipError_t launch_decode_kv(const DecodeArgs& a, int D, int B, int G, int64_t upper, hipStream_t s) {
+hipError_t launch_decode_kv(const DecodeArgs& a, int D, int B, int G, int64_t upper, hipStream_t s,
+                            const LaunchEvents& ev) {
 #define PA_DEC_CASE(d, b, g) \
-  if (D == d && B == b && G == g) return launch_decode_t<KV, d, b, g>(a, upper, s);
+  if (D == d && B == b && G == g) return launch_decode_t<KV, d, b, g>(a, upper, s, ev);
 #define PA_DEC_G(d, b) PA_DEC_CASE(d, b, 1) PA_DEC_CASE(d, b, 2) PA_DEC_CASE(d, b, 4) PA_DEC_CASE(d, b, 8)
   PA_DEC_G(64, 16)
   PA_DEC_G(64, 32)

@@ -91,8 +91,15 @@ hipError_t launch_copy_blocks(const CopyArgs& a, int num_pairs, hipStream_t s);
 // elem_bytes 1, 2 or 4; grid num_seqs x max_blocks_used.
 hipError_t launch_pack_kv(const PackArgs& a, int elem_bytes, int num_seqs, int max_blocks_used, hipStream_t s);
 // Returns hipErrorInvalidValue for a combination without a compiled kernel.
+// Events a launch records with its kernel's own start and end timestamps
+// (hipExtLaunchKernel); both null: a plain launch.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 hipError_t launch_decode(const DecodeArgs& a, int kv_kind, int head_dim, int block_size, int group,
-                         int64_t upper_units, hipStream_t s);
+                         int64_t upper_units, hipStream_t s, const LaunchEvents& ev);
 // bf16 cache, head_dim 128; hipErrorInvalidValue for an uncompiled combination.
 // kv_kind: KV_BF16 or KV_FP8 (bf16 queries and output in both cases).
 hipError_t launch_prefill_chunk(const PrefillArgs& a, int kv_kind, int block_size, int group, hipStream_t s);

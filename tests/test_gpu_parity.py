@@ -213,6 +213,32 @@ def test_decode_repeated_calls_reuse_the_workspace():
                     first[(i, part)] = o
 
 
+def test_decode_timing_hook_stamps_one_kernel():
+    """pa_decode_time_next: the armed call gives the same bits as an unarmed
+    one and stamps its events with a positive kernel duration; the next,
+    unarmed call leaves the events as they were."""
+    from paged_kv_attention_26_amd import binding as pa, runner
+    say("[gpu] decode timing hook")
+    batch = SMALL["c2s"]()
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    ref = runner.decode_step(g).clone()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    torch.cuda.synchronize()
+    pa.time_next_decode(e0, e1)
+    out = runner.decode_step(g).clone()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1)
+    say(f"      kernel {t * 1e3:.1f} us")
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert 0.0 < t < 1000.0
+    runner.decode_step(g)
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) == t
+
+
 def test_block_permutation_leaves_output_bit_identical():
     from paged_kv_attention_26_amd import runner
     a = W.config2(small=True)
