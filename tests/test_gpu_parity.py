@@ -137,22 +137,31 @@ def slot_pattern(rng, num_blocks, B, T):
     return np.asarray(out[:T], dtype=np.int32)
 
 
+@pytest.mark.parametrize("T", [700, 1, 37, 128, 129])
 @pytest.mark.parametrize("kv,B,D", [("bf16", 16, 128), ("bf16", 32, 64), ("f32", 16, 64), ("f32", 32, 128),
-                                    ("fp8", 16, 128), ("fp8", 32, 128)])
-def test_store_slot_patterns_bit_exact(kv, B, D):
+                                    ("fp8", 16, 128), ("fp8", 32, 128), ("fp8raw", 16, 128), ("fp8raw", 32, 64)])
+def test_store_slot_patterns_bit_exact(kv, B, D, T):
     """pa_store_kv with arbitrary slot patterns (whole and partial blocks,
     misaligned and skipped tokens) against the oracle's scatter, bit for bit
-    over the whole poisoned pool."""
+    over the whole poisoned pool.  Batches of at most 128 tokens take the
+    one-wave-per-row store, larger ones the 64-token tiles; fp8raw stores
+    e4m3 codes as they are."""
     from oracle import paged
     from paged_kv_attention_26_amd import binding as pa
-    rng = np.random.default_rng(4242 + B + D)
-    NB, H, T = 96, 2, 700
+    rng = np.random.default_rng(4242 + B + D + T)
+    NB, H = 96, 2
     slots = slot_pattern(rng, NB, B, T)
     T = len(slots)
     say(f"[gpu] store slot patterns {kv} B{B} d{D}: {T} tokens, {int((slots < 0).sum())} skipped")
     x = rng.standard_normal((2, T, H, D)).astype(np.float32)
     scale = (rng.random(H).astype(np.float32) * 0.5 + 0.25) if kv == "fp8" else None
-    if kv == "f32":
+    if kv == "fp8raw":
+        kin, vin = (rng.integers(0, 256, (2, T, H, D)).astype(np.uint8))
+        scale = np.ones(H, np.float32)                    # the cache's scales; a raw store ignores them
+        kt = torch.from_numpy(kin).cuda()
+        vt = torch.from_numpy(vin).cuda()
+        kv = in_dt = "fp8"
+    elif kv == "f32":
         kin, vin = x[0], x[1]
         kt, vt = torch.from_numpy(kin).cuda(), torch.from_numpy(vin).cuda()
         in_dt = "f32"
