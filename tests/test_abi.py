@@ -72,6 +72,7 @@ def decode_call(c, **kw):
     (dict(c=cache(), ws_bytes=16), L.PA_ERR_WORKSPACE),
     (dict(c=cache(), lens=None), L.PA_ERR_NULL),
     (dict(c=cache(), S=-1), L.PA_ERR_SHAPE),
+    (dict(c=cache(), S=8193), L.PA_ERR_SHAPE),                       # more sequences than the LDS prefix holds
     (dict(c=cache(), scale=float("nan")), L.PA_ERR_SHAPE),
     (dict(c=cache(), scale=0.0), L.PA_ERR_SHAPE),
     (dict(c=cache(), scale=-0.125), L.PA_ERR_SHAPE),
@@ -114,6 +115,7 @@ def test_pack_rejects_bad_arguments():
                               a["S"], a["max_len"], a["k"], a["v"], None)
     assert call(None) == L.PA_ERR_NULL
     assert call(c, S=-1) == L.PA_ERR_SHAPE
+    assert call(c, S=8193) == L.PA_ERR_SHAPE
     assert call(c, max_len=-5) == L.PA_ERR_SHAPE
     assert call(c, width=3) == L.PA_ERR_SHAPE        # 64 tokens need 4 blocks
     assert call(c, k=None) == L.PA_ERR_NULL

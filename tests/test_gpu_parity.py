@@ -86,6 +86,18 @@ def many_batch():
                          prior_lens=prior, new_lens=new, is_chunk=np.zeros(len(lens), bool), rng=rng)
 
 
+def max_seqs_batch():
+    """8192 sequences, the most one call takes (the decode kernel's prefix
+    over sequences lives in LDS), of 0 to 40 tokens."""
+    rng = np.random.default_rng(80)
+    lens = rng.integers(0, 41, 8192)
+    lens[::61] = 0
+    prior = np.maximum(lens - 1, 0)
+    new = (lens > 0).astype(np.int64)
+    return W.paged_batch("maxseq-bf16", 80, kv_dtype="bf16", io_dtype="bf16", Hq=8, Hkv=2, d=64, B=16,
+                         prior_lens=prior, new_lens=new, is_chunk=np.zeros(len(lens), bool), rng=rng)
+
+
 SMALL = {
     "c1": lambda: W.config1(),
     "c2s": lambda: W.config2(small=True),
@@ -195,6 +207,31 @@ def test_decode_matches_oracle(name, part):
     err = np.max(np.abs(got - ref))
     say(f"      max abs err {err:.3e}")
     assert err < TOL[batch.kv_dtype]
+
+
+@pytest.mark.parametrize("part", [0, 1024])
+def test_decode_at_the_sequence_limit(part):
+    """The largest batch one call takes (8192 sequences), at the default and
+    at the largest partition (64 blocks of 16): store bit-exact over the
+    whole pool, every output against the oracle, and the pack of every
+    sequence bit-exact."""
+    from oracle import paged
+    from paged_kv_attention_26_amd import runner
+    say(f"[gpu] decode at the sequence limit, partition {part}")
+    batch = max_seqs_batch()
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    got = out_f64(runner.decode_step(g, partition_tokens=part))
+    k, v = runner.pack_all(g)
+    torch.cuda.synchronize()
+    st = OS.build(batch)
+    assert np.array_equal(bits(g.cache.k_cache, "bf16"), oracle_bits(st.kc, "bf16"))
+    assert np.array_equal(bits(g.cache.v_cache, "bf16"), oracle_bits(st.vc, "bf16"))
+    err = np.max(np.abs(got - OS.decode_ref(batch, st)))
+    say(f"      max abs err {err:.3e}")
+    assert err < TOL["bf16"]
+    kr, vr = paged.pack_kv(st.kc, st.vc, st.tables, batch.total_lens)
+    assert np.array_equal(bits(k, "bf16"), oracle_bits(kr, "bf16")) and np.array_equal(bits(v, "bf16"), oracle_bits(vr, "bf16"))
 
 
 def test_decode_repeated_calls_reuse_the_workspace():
@@ -543,7 +580,9 @@ def _long_context(B):
 def test_decode_full_long_context_sampled(B):
     """Long-context decode at full size (128 seqs, 713k tokens, contexts up
     to 28k) with 512-token partitions, as benchmarked: the longest, the
-    shortest and six seeded sequences against the oracle one by one."""
+    shortest and six seeded sequences against the oracle one by one.  The
+    bulk store that filled the pool (the bench's bulk-store case) is checked
+    bit for bit over the whole poisoned pool."""
     from oracle import paged
     from paged_kv_attention_26_amd import binding as pa, runner
     say(f"[gpu] decode full long context B{B}")
@@ -553,8 +592,11 @@ def test_decode_full_long_context_sampled(B):
     ws = pa.decode_workspace(1, 1, batch.head_dim, 1, 512)
     got = out_f64(runner.decode_step(g, partition_tokens=512, workspace=ws))
     torch.cuda.synchronize()
-    del g
     st = OS.build(batch)
+    assert np.array_equal(bits(g.cache.k_cache, "bf16"), oracle_bits(st.kc, "bf16"))
+    assert np.array_equal(bits(g.cache.v_cache, "bf16"), oracle_bits(st.vc, "bf16"))
+    say("      whole pool bit-exact after the bulk store")
+    del g
     lens = batch.total_lens
     pick = {int(np.argmax(lens)), int(np.argmin(lens))}
     pick |= set(int(x) for x in np.random.default_rng(7).choice(len(lens), 6, replace=False))
