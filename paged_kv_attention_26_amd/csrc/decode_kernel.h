@@ -106,13 +106,20 @@ __device__ __forceinline__ int owner_wave(int64_t u, int64_t U, int64_t W) {
 }
 
 // Exclusive prefix of the partitions per sequence, built in LDS by the
-// whole workgroup: s_prefix[s] = sum over s' < s, s_prefix[S] = total.
-__device__ __forceinline__ void build_prefix(const int32_t* lens, int S, int PT, int* s_prefix, int* s_tmp) {
+// whole workgroup: s_prefix[s] = sum over s' < s, s_prefix[S] = total.  The
+// lengths themselves are kept in LDS too (s_len[s] = max(0, lens[s])), so
+// that no wave goes back to memory for its sequences' lengths.
+__device__ __forceinline__ void build_prefix(const int32_t* lens, int S, int PT, int* s_prefix, int* s_len,
+                                             int* s_tmp) {
   const int tid = threadIdx.x;
   const int per = (S + 255) / 256;
   const int i0 = tid * per, i1 = min(S, i0 + per);
   int local = 0;
-  for (int i = i0; i < i1; ++i) local += units_of(lens[i], PT);
+  for (int i = i0; i < i1; ++i) {
+    const int L = max(0, lens[i]);
+    s_len[i] = L;
+    local += units_of(L, PT);
+  }
   s_tmp[tid] = local;
   __syncthreads();
   for (int off = 1; off < 256; off <<= 1) {
@@ -124,7 +131,7 @@ __device__ __forceinline__ void build_prefix(const int32_t* lens, int S, int PT,
   int run = tid ? s_tmp[tid - 1] : 0;
   for (int i = i0; i < i1; ++i) {
     s_prefix[i] = run;
-    run += units_of(lens[i], PT);
+    run += units_of(s_len[i], PT);
   }
   if (tid == 255) s_prefix[S] = s_tmp[255];
   __syncthreads();
@@ -245,14 +252,15 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
                                                      const int32_t* __restrict__ context_lens) {
   using C = DecCfg<KV, D, B, G>;
   using LoadT = typename C::LoadT;
-  extern __shared__ int s_prefix[];                       // [num_seqs + 1]
+  extern __shared__ int s_prefix[];                       // [num_seqs + 1], then s_len [num_seqs]
   __shared__ int s_tmp[256];
   __shared__ float s_score[4][C::CH * G];                 // [token][head] per wave
   __shared__ __attribute__((aligned(16))) uint32_t s_p[4][C::CH * G];   // probabilities per wave
 
   const int S = a.num_seqs;
   const int PT = a.part_tokens;
-  build_prefix(context_lens, S, PT, s_prefix, s_tmp);
+  int* s_len = s_prefix + S + 1;
+  build_prefix(context_lens, S, PT, s_prefix, s_len, s_tmp);
 
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);                // wave-uniform, so all range math stays scalar
@@ -288,7 +296,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
     bool live, any;             // any: some step of the range was ever found
   };
   auto seg_setup = [&](Cursor& c) {                          // derive the segment's steps
-    const int L = max(0, context_lens[c.seq]);
+    const int L = uniform(s_len[c.seq]);
     const int nu = units_of(L, PT);
     c.p_end = int(min<int64_t>(nu, c.part + (u_end - c.u)));
     const int t_begin = c.part * PT, t_end = min(L, c.p_end * PT);
@@ -374,7 +382,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
   int seq = find_seq(s_prefix, S, int(u / Hkv));
   int kvh, part;
   {
-    const int nu = units_of(context_lens[seq], PT);
+    const int nu = units_of(uniform(s_len[seq]), PT);
     const int r = int(u - int64_t(s_prefix[seq]) * Hkv);
     kvh = uniform(r / nu);
     part = uniform(r - kvh * nu);
@@ -446,7 +454,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
   bool first = true;
   bool q_ready = false;                                      // qfn / qpn hold this segment's query
   for (;;) {                                                 // one (sequence, kv head) segment per pass
-    const int L = max(0, context_lens[seq]);
+    const int L = uniform(s_len[seq]);
     const int nu = units_of(L, PT);
     const int p_end = int(min<int64_t>(nu, part + (u_end - u)));
     const bool whole = part == 0 && p_end == nu;
@@ -727,7 +735,7 @@ hipError_t launch_with_events(K kern, dim3 grid, dim3 block, size_t lds, hipStre
 template <int KV, int D, int B, int G>
 hipError_t launch_decode_t(const DecodeArgs& a0, int64_t upper_units, hipStream_t s, const LaunchEvents& ev) {
   auto kern = decode_kernel<KV, D, B, G>;
-  const size_t lds = size_t(a0.num_seqs + 1) * sizeof(int);
+  const size_t lds = size_t(2 * a0.num_seqs + 1) * sizeof(int);
   static int cached_occ = -1;
   static size_t cached_lds = 0;
   if (cached_occ < 0 || cached_lds != lds) {
