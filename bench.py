@@ -203,6 +203,30 @@ def mixed_batch(pa, runner, W, out):
         fl += 4 * b.head_dim * b.num_q_heads * (int(n) * int(P) + int(n) * (int(n) + 1) // 2)
     out["mixed_prefill_chunk"] = dict(TFLOPs=round(fl / med / 1e9, 1), ms=round(med, 4),
                                       frac=round(fl / med / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4), flops=fl)
+
+    # The whole step: store the 4096 chunk rows and 64 decode tokens, then the
+    # two attention calls, one after the other on one stream ...
+    def step_one_stream():
+        runner.store_step(g)
+        runner.chunk_step(g)
+        runner.decode_step(g, workspace=ws)
+    med, _, _ = timed_calls(step_one_stream, 20)
+    out["mixed_step"] = dict(ms=round(med, 4), note="store + prefill + decode, one stream")
+    # ... and with the decode on a second stream (default priority), which
+    # waits for the store and runs beside the prefill.
+    import torch
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+
+    def step_two_streams():
+        runner.store_step(g)
+        side.wait_stream(main)
+        runner.chunk_step(g)
+        with torch.cuda.stream(side):
+            runner.decode_step(g, workspace=ws)
+        main.wait_stream(side)
+    med, _, _ = timed_calls(step_two_streams, 20)
+    out["mixed_step_two_streams"] = dict(ms=round(med, 4), note="decode on a second stream beside the prefill")
     del g
     # the same chunks over an fp8 e4m3 cache (per-head scales; bf16 matrix cores)
     b8 = W.config4(kv_dtype="fp8")
