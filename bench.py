@@ -56,6 +56,12 @@ def kv_bytes(lens, hkv, d, es):
     return int(np.sum(lens)) * 2 * hkv * d * es
 
 
+def device_info(torch):
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2**30, 1)}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,7 +246,9 @@ def mixed_batch(pa, runner, W, out):
 def cpu_baseline(batch, budget_s=10.0):
     """The oracle (plain fp64 numpy) on a bounded sample of the workload: it
     decodes the batch's sequences one by one, pass after pass, for about
-    budget_s seconds, and reports the KV bytes attended per second."""
+    budget_s seconds, and reports the KV bytes attended per second.  Measured
+    twice: with every BLAS thread the host gives it, and on one thread.
+    Returns (all threads, one thread)."""
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from oracle import paged
     from tests import oracle_setup as OS
@@ -248,24 +256,36 @@ def cpu_baseline(batch, budget_s=10.0):
     dec = np.flatnonzero(~batch.is_chunk)
     tables = OS.table_array([st.tables[i] for i in dec], st.pad_block)
     lens = batch.total_lens[dec]
-    seqs, byt, tokens = 0, 0, 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        s = seqs % len(dec)
-        paged.decode_attention(st.kc, st.vc, batch.kv_dtype, batch.q_decode[s:s + 1], batch.io_dtype,
-                               tables[s:s + 1], lens[s:s + 1], batch.scale)
-        byt += kv_bytes(lens[s:s + 1], batch.num_kv_heads, batch.head_dim, 2)
-        tokens += int(lens[s])
-        seqs += 1
-    dt = time.perf_counter() - t0
-    try:                                   # threads the oracle's BLAS calls actually run on
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
-    return dict(value=round(byt / dt / 1e9, 4), unit="GB/s", cores=int(threads), kind="oracle",
-                sample=f"fp64 numpy decode of the {len(dec)} sequences, {seqs / len(dec):.1f} passes "
-                       f"({seqs} sequence decodes, {tokens} KV tokens x {batch.num_kv_heads} kv heads) in {dt:.1f} s")
+
+    def run():
+        seqs, byt, tokens = 0, 0, 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            s = seqs % len(dec)
+            paged.decode_attention(st.kc, st.vc, batch.kv_dtype, batch.q_decode[s:s + 1], batch.io_dtype,
+                                   tables[s:s + 1], lens[s:s + 1], batch.scale)
+            byt += kv_bytes(lens[s:s + 1], batch.num_kv_heads, batch.head_dim, 2)
+            tokens += int(lens[s])
+            seqs += 1
+        dt = time.perf_counter() - t0
+        try:                               # threads the oracle's BLAS calls actually run on
+            from threadpoolctl import threadpool_info
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:
+            threads = 1
+        return dict(value=round(byt / dt / 1e9, 4), unit="GB/s", cores=int(threads), kind="oracle",
+                    sample=f"fp64 numpy decode of the {len(dec)} sequences, {seqs / len(dec):.1f} passes "
+                           f"({seqs} sequence decodes, {tokens} KV tokens x {batch.num_kv_heads} kv heads) "
+                           f"in {dt:.1f} s")
+
+    every = run()
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            one = run()
+    except ImportError:
+        one = None
+    return every, one
 
 
 def main():
@@ -358,6 +378,7 @@ def main():
                    "global_batch": int(len(lens_all)), "seq_len": int(np.max(lens_all)),
                    "kv_tokens": int(np.sum(lens_all)), "layer_caches": args.layers,
                    "partition_tokens": args.partition or 64, "parallelism": "single-gpu"},
+        "device": device_info(torch),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": decode_traffic(),
                      "kernel": "pa::decode_kernel<bf16, d128, B16, G4>",
@@ -370,7 +391,9 @@ def main():
         torch.cuda.empty_cache()
         rec["extras"] = extras(pa, runner, W, torch)
     if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(W.config2())
+        rec["cpu_baseline"], one = cpu_baseline(W.config2())
+        if one is not None:
+            rec["cpu_baseline_single_thread"] = one
     print(json.dumps(rec), flush=True)
 
 
