@@ -11,12 +11,13 @@
 // fp32 accumulate):
 //  * A wave owns 32 query rows of one query head; the four waves of a
 //    workgroup share a kv head (the G = 4 heads of a query tile, or more
-//    tiles of fewer heads).  The workgroup stages each 32-key K / V^T tile once into LDS
-//    (K chunks XOR-swizzled, V^T rows padded, so that the MFMA operand reads
-//    are free of bank conflicts),
-//    double-buffered: the next tile's global loads fly while the current
-//    tile's MFMAs run, one barrier per tile.  Block ids come through the
-//    scalar cache.  Two workgroups share each CU, so the two waves on a
+//    tiles of fewer heads).  The workgroup stages each 32-key K / V^T tile
+//    once into LDS, swizzled so that the MFMA operand reads are free of bank
+//    conflicts.  A bf16 cache is loaded straight into LDS (16-byte loads to
+//    LDS, no registers) through a ring of three buffers, two tiles ahead of
+//    their MFMAs; an fp8 cache is loaded into registers, converted to bf16
+//    and written to two buffers.  One barrier per tile.  Block ids come
+//    through the scalar cache.  Two workgroups share each CU, so the two waves on a
 //    SIMD belong to different workgroups and do not pass their barriers
 //    together: one's softmax can overlap the other's MFMAs.
 //  * Scores are formed transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16
@@ -68,7 +69,15 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
   constexpr int VROW = KT * 2 + 16;      // LDS bytes per head-dim row of the transposed value tile
   constexpr int KBUF = KT * KROW;
   constexpr int BUF = KBUF + D * VROW;
-  __shared__ __attribute__((aligned(16))) char smem[2][BUF];   // double-buffered K / V^T tile
+  // A bf16 cache is staged straight from memory into LDS (16-byte loads to
+  // LDS) through a ring of three unpadded buffers; an fp8 cache goes through
+  // registers, converted to bf16, into two padded buffers.
+  constexpr bool DIRECT = KV == KV_BF16;
+  constexpr int RBUF = KBUF + D * KT * 2;                  // ring buffer: K tile, then V^T tile
+  __shared__ __attribute__((aligned(16))) char smem[2][DIRECT ? 16 : BUF];   // double-buffered (fp8)
+  __shared__ __attribute__((aligned(16))) char ring0[DIRECT ? RBUF : 16];
+  __shared__ __attribute__((aligned(16))) char ring1[DIRECT ? RBUF : 16];
+  __shared__ __attribute__((aligned(16))) char ring2[DIRECT ? RBUF : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -196,6 +205,43 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
     id1 = table[min(b0 + 1, kmax / B)];
   };
 
+  // Ring layout.  A load to LDS puts lane l's 16 bytes at the wave's base +
+  // 16 l, so the layout is chosen per LDS position and each lane loads the
+  // chunk that belongs there.  K: position 16 r + (c ^ kswz(r)) holds chunk c
+  // of key row r (the padded layout's swizzle, rows of 256 bytes).  V^T:
+  // position 4 r + (g ^ vphi(r)) holds keys 8g .. 8g + 7 of head dim r, so
+  // that the operand reads (lane n: dim 32 dt + n, one g per half wave) fall
+  // on distinct 16-byte bank groups in every 8 and every 16 lanes.
+  auto vphi = [](int r) { return ((r >> 1) ^ (r >> 3)) & 3; };
+  auto v_pos = [&](int r, int g) { return 4 * r + (g ^ vphi(r)); };
+  // thread tid fills positions tid and tid + 256 of each tile (lane l of wave
+  // w writes position 256 j + 64 w + l)
+  uint64_t dk_off[2], dv_off[2];
+  bool dk_hi[2], dv_hi[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int pk = tid + 256 * j;
+    const int row = pk >> 4, colc = (pk & 15) ^ kswz(row);
+    dk_hi[j] = B != KT && row >= B;
+    dk_off[j] = uint64_t(((row % B) * D + colc * 8) * 2);
+    const int dim = pk >> 2, g = (pk & 3) ^ vphi(pk >> 2);
+    dv_hi[j] = B != KT && 8 * g >= B;
+    dv_off[j] = uint64_t((dim * B + (8 * g) % B) * 2);
+  }
+  auto direct_stage = [&](char* base, int id0, int id1) __attribute__((always_inline)) {
+    const uint64_t t0_ = (uint64_t(uint32_t(id0)) * uint32_t(Hkv) + uint32_t(kvh)) * kBlockTile;
+    const uint64_t t1_ = (uint64_t(uint32_t(id1)) * uint32_t(Hkv) + uint32_t(kvh)) * kBlockTile;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      char* kb = base + (256 * j + 64 * w) * 16;
+      char* vb = base + KBUF + (256 * j + 64 * w) * 16;
+      __builtin_amdgcn_global_load_lds(kpool + (dk_hi[j] ? t1_ : t0_) + dk_off[j],
+                                       (__attribute__((address_space(3))) void*)kb, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vpool + (dv_hi[j] ? t1_ : t0_) + dv_off[j],
+                                       (__attribute__((address_space(3))) void*)vb, 16, 0, 0);
+    }
+  };
+
   // ---- Q^T as 8 B operands (k = 16 head dims each): row q0 + t, dims 16s + 8hh .. + 7
   uint4 qb[8];
   {
@@ -279,7 +325,8 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          va[dt][ks] = *reinterpret_cast<const uint4*>(sb + KBUF + (32 * dt + n) * VROW + (16 * ks + 8 * hh) * 2);
+          va[dt][ks] = DIRECT ? *reinterpret_cast<const uint4*>(sb + KBUF + v_pos(32 * dt + n, 2 * ks + hh) * 16)
+                              : *reinterpret_cast<const uint4*>(sb + KBUF + (32 * dt + n) * VROW + (16 * ks + 8 * hh) * 2);
       if (k0 + KT > key_end) {                           // zero V rows of keys past the end (NaN poison)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -303,8 +350,46 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
   };
 
   const int last = n_tiles_wg - 1;
-  typename Raw::T sa_k0{}, sa_v0{}, sb_k0{}, sb_v0{}, sa_k1{}, sa_v1{}, sb_k1{}, sb_v1{};
   int j0, j1;
+  if constexpr (DIRECT) {
+    // Ring of three buffers.  Tile kt + 2 is loaded into the buffer that
+    // held tile kt - 1, which every wave finished reading before the barrier
+    // that closed tile kt - 1.  A thread has four loads per tile, so once
+    // only its four newest are in flight (vmcnt(4)), its part of tile kt + 1
+    // is in LDS, and after the barrier all of it is.  The barrier is a plain
+    // s_barrier between compiler-only fences: a __syncthreads() would also
+    // wait for tile kt + 2.  Each buffer is a distinct array named
+    // statically, so the compiler does not take loads into one for writes to
+    // the one being read (it would wait for them before every LDS read).
+#define PA_RING_SYNC()                                                                                 \
+    __builtin_amdgcn_s_waitcnt(0x0F74); /* vmcnt(4) */                                                 \
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);                                                           \
+    __builtin_amdgcn_s_barrier();                                                                      \
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    tile_ids(0, j0, j1);
+    direct_stage(ring0, j0, j1);
+    tile_ids(min(1, last), j0, j1);
+    direct_stage(ring1, j0, j1);
+    tile_ids(min(2, last), j0, j1);
+    __builtin_amdgcn_s_waitcnt(0x0F74);                     // vmcnt(4): tile 0 is in LDS
+    __syncthreads();                                          // (once: also settles the query loads)
+#define PA_RING_STEP(KT_, NEXT, CUR)                                                                   \
+    direct_stage(NEXT, j0, j1);                                                                        \
+    tile_ids(min((KT_) + 3, last), j0, j1);                                                            \
+    compute_tile((KT_), CUR);                                                                          \
+    PA_RING_SYNC()
+    for (int kt = 0; kt < n_tiles_wg; kt += 3) {
+      PA_RING_STEP(kt, ring2, ring0)
+      if (kt + 1 >= n_tiles_wg) break;
+      PA_RING_STEP(kt + 1, ring0, ring1)
+      if (kt + 2 >= n_tiles_wg) break;
+      PA_RING_STEP(kt + 2, ring1, ring2)
+    }
+#undef PA_RING_STEP
+#undef PA_RING_SYNC
+    __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0): no load into LDS outlives the loop
+  } else {
+  typename Raw::T sa_k0{}, sa_v0{}, sb_k0{}, sb_v0{}, sa_k1{}, sa_v1{}, sb_k1{}, sb_v1{};
   tile_ids(0, j0, j1);
   PA_STAGE_LOAD(sa_, 0, j0, j1);
   tile_ids(min(1, last), j0, j1);
@@ -324,6 +409,7 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
     compute_tile(kt + 1, smem[1]);
     PA_STAGE_STORE(sa_, 0);                                  // tile kt + 2
     __syncthreads();
+  }
   }
 #undef PA_STAGE_LOAD
 #undef PA_STAGE_STORE
