@@ -226,8 +226,8 @@ constexpr int kStoreRowsMaxTokens = 128;
 // The store of a few scattered tokens (a decode step: one new token per
 // sequence), where the time is latency, not bandwidth.  One wave per (token,
 // kv head), so a 32-token step spreads over 256 waves instead of eight
-// workgroups.  Every load of the wave (its slot, its key row as 16-byte
-// chunks, its value row one element per lane) is issued before any store,
+// workgroups.  Every load of the wave (its slot, fp8 scales, its key row as
+// 16-byte chunks, its value row one element per lane) is issued before any store,
 // so the wave pays one memory round trip; then the key row goes out as
 // 16-byte chunks and the value elements go to their transposed places
 // (head dim d at element d * block_size + offset of the tile).
@@ -247,6 +247,11 @@ __global__ void __launch_bounds__(256) store_rows_kernel(StoreArgs a) {
   const char* vrow = static_cast<const char*>(a.v_new) + (size_t(t) * H + h) * D * IN_ES;
 
   const int slot = a.slot_mapping[t];
+  float ksc = 1.f, vsc = 1.f;
+  if constexpr (KV == KV_FP8) {
+    ksc = a.k_scale[h];
+    vsc = a.v_scale[h];
+  }
   const uint4 kx = *reinterpret_cast<const uint4*>(krow + size_t(min(lane, cpr - 1)) * 16);
   uint32_t vx[2];
 #pragma unroll
@@ -258,11 +263,6 @@ __global__ void __launch_bounds__(256) store_rows_kernel(StoreArgs a) {
   }
   if (slot < 0) return;
   const int blk = slot / BS, off = slot % BS;
-  float ksc = 1.f, vsc = 1.f;
-  if constexpr (KV == KV_FP8) {
-    ksc = a.k_scale[h];
-    vsc = a.v_scale[h];
-  }
   char* kdst = static_cast<char*>(a.k_cache) + ((size_t(blk) * H + h) * BS + off) * size_t(D) * OUT_ES;
   char* vdst = static_cast<char*>(a.v_cache) + (size_t(blk) * H + h) * size_t(D) * BS * OUT_ES + size_t(off) * OUT_ES;
   if (lane < cpr) {
