@@ -75,8 +75,11 @@ struct DecCfg {
   static constexpr int DPL = 64 / LPD;                            // head dims per value load
   static constexpr int KLB = B / RPL;                             // key loads per block
   static constexpr int VLB = D / DPL;                             // value loads per block
-  // tokens per step: the configured step rounded up to whole blocks (<= 64)
-  static constexpr int CH = ((PA_DECODE_STEP_TOKENS + B - 1) / B) * B;
+  // tokens per step: the configured step rounded up to whole blocks (<= 64);
+  // 32 for an fp32 cache at head_dim 128 with four or more heads per group,
+  // whose 64-token K and V tiles alone would fill the 256 registers
+  static constexpr int STEP = (F32 && D == 128 && G >= 4) ? 32 : PA_DECODE_STEP_TOKENS;
+  static constexpr int CH = ((STEP + B - 1) / B) * B;
   static constexpr int BPC = CH / B;                              // blocks per step
   using LoadT = typename std::conditional<LBYTES == 16, uint4, uint2>::type;
   static_assert(LPR >= G && LPR <= 64 && (64 % LPR) == 0, "key row mapping");

@@ -234,6 +234,33 @@ def test_decode_at_the_sequence_limit(part):
     assert np.array_equal(bits(k, "bf16"), oracle_bits(kr, "bf16")) and np.array_equal(bits(v, "bf16"), oracle_bits(vr, "bf16"))
 
 
+@pytest.mark.parametrize("B", [16, 32])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_f32_head_dim_128(G, B):
+    """An fp32 cache at head_dim 128 (32-token steps from four heads per
+    group up): ragged lengths across several steps and partitions, against
+    the oracle within the fp32 tolerance, at the default partition and at
+    128-token partitions."""
+    from paged_kv_attention_26_amd import runner
+    rng = np.random.default_rng(600 + 10 * G + B)
+    lens = np.concatenate([[0, 1, 31, 32, 33, 64, 65, 700], rng.integers(1, 900, 9)])
+    prior = np.maximum(lens - 1, 0)
+    new = (lens > 0).astype(np.int64)
+    batch = W.paged_batch(f"f32-d128-g{G}-b{B}", 600 + G, kv_dtype="f32", io_dtype="f32", Hq=2 * G, Hkv=2, d=128,
+                          B=B, prior_lens=prior, new_lens=new, is_chunk=np.zeros(len(lens), bool), rng=rng)
+    say(f"[gpu] decode f32 d128 G{G} B{B}")
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    st = OS.build(batch)
+    ref = OS.decode_ref(batch, st)
+    for part in (0, 128):
+        got = out_f64(runner.decode_step(g, partition_tokens=part))
+        torch.cuda.synchronize()
+        err = np.max(np.abs(got - ref))
+        say(f"      partition {part}: max abs err {err:.3e}")
+        assert err < TOL["f32"]
+
+
 def test_decode_repeated_calls_reuse_the_workspace():
     """Calls of different shapes and partition sizes, interleaved on one
     workspace, repeat bit-identically, and every call leaves the per-item
