@@ -261,6 +261,33 @@ def test_decode_f32_head_dim_128(G, B):
         assert err < TOL["f32"]
 
 
+@pytest.mark.parametrize("B", [16, 32])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_fp8_head_dim_64(G, B):
+    """An fp8 cache at head_dim 64 (up to four waves per SIMD, so launches
+    of up to 4096 waves): ragged lengths, per-head scales, against the oracle
+    at the default and at 128-token partitions."""
+    from paged_kv_attention_26_amd import runner
+    rng = np.random.default_rng(700 + 10 * G + B)
+    lens = np.concatenate([[0, 1, 63, 64, 65, 1100], rng.integers(1, 1500, 10)])
+    prior = np.maximum(lens - 1, 0)
+    new = (lens > 0).astype(np.int64)
+    batch = W.paged_batch(f"fp8-d64-g{G}-b{B}", 700 + G, kv_dtype="fp8", io_dtype="bf16", Hq=4 * G, Hkv=4, d=64,
+                          B=B, prior_lens=prior, new_lens=new, is_chunk=np.zeros(len(lens), bool), rng=rng)
+    say(f"[gpu] decode fp8 d64 G{G} B{B}")
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    st = OS.build(batch)
+    assert np.array_equal(bits(g.cache.k_cache, "fp8"), st.kc) and np.array_equal(bits(g.cache.v_cache, "fp8"), st.vc)
+    ref = OS.decode_ref(batch, st)
+    for part in (0, 128):
+        got = out_f64(runner.decode_step(g, partition_tokens=part))
+        torch.cuda.synchronize()
+        err = np.max(np.abs(got - ref))
+        say(f"      partition {part}: max abs err {err:.3e}")
+        assert err < TOL["fp8"]
+
+
 def test_decode_repeated_calls_reuse_the_workspace():
     """Calls of different shapes and partition sizes, interleaved on one
     workspace, repeat bit-identically, and every call leaves the per-item
@@ -468,6 +495,29 @@ CHUNKS = {
                                           kv="fp8"),
     "fp8-verify": lambda: chunk_batch("fp8-verify", [0, 15, 1023, 4100], [5, 8, 1, 5], kv="fp8"),
 }
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("B", [16, 32])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_prefill_every_compiled_shape(kv, B, G):
+    """Every (cache dtype, block size, group) the chunked prefill compiles,
+    in both of its kernels: chunks longer than 32 / G tokens (tiles of 32
+    query rows of one head) and chunks of at most 32 / G tokens (verification:
+    (head, token) columns), on prefixes that end inside a block and at block
+    ends, against the oracle."""
+    from paged_kv_attention_26_amd import runner
+    for form, P, q in (("chunks", [0, 37, 160, 500], [70, 33, 97, 1]), ("verify", [5, 64, 900], [32 // G, 1, max(1, 16 // G)])):
+        batch = chunk_batch(f"every-{form}-{kv}-b{B}-g{G}", P, q, B=B, Hq=2 * G, Hkv=2, seed=900 + G + B, kv=kv)
+        say(f"[gpu] prefill {batch.name}")
+        g = runner.prepare(batch)
+        runner.store_step(g)
+        got = out_f64(runner.chunk_step(g))
+        torch.cuda.synchronize()
+        st = OS.build(batch)
+        err = np.max(np.abs(got - OS.chunk_ref(batch, st)))
+        say(f"      max abs err {err:.3e}")
+        assert np.all(np.isfinite(got)) and err < TOL[kv]
 
 
 @pytest.mark.parametrize("name", list(CHUNKS))
