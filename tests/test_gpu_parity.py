@@ -288,6 +288,36 @@ def test_decode_fp8_head_dim_64(G, B):
         assert err < TOL["fp8"]
 
 
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("B", [16, 32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
+def test_every_compiled_decode_shape(kv, d, B, G):
+    """Every (cache dtype, head_dim, block size, group) the decode compiles,
+    on a small ragged batch: the store bit-exact over the whole pool, the
+    decode against the oracle, the pack bit-exact."""
+    from oracle import paged
+    from paged_kv_attention_26_amd import runner
+    rng = np.random.default_rng(800 + 97 * G + B + d)
+    lens = np.concatenate([[0, 1, B - 1, B, B + 1, 200], rng.integers(1, 300, 4)])
+    prior = np.maximum(lens - 1, 0)
+    new = (lens > 0).astype(np.int64)
+    io = "f32" if kv == "f32" else "bf16"
+    batch = W.paged_batch(f"every-{kv}-d{d}-b{B}-g{G}", 800 + G, kv_dtype=kv, io_dtype=io, Hq=2 * G, Hkv=2, d=d,
+                          B=B, prior_lens=prior, new_lens=new, is_chunk=np.zeros(len(lens), bool), rng=rng)
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    got = out_f64(runner.decode_step(g))
+    k, v = runner.pack_all(g)
+    torch.cuda.synchronize()
+    st = OS.build(batch)
+    assert np.array_equal(bits(g.cache.k_cache, kv), oracle_bits(st.kc, kv))
+    assert np.array_equal(bits(g.cache.v_cache, kv), oracle_bits(st.vc, kv))
+    assert np.max(np.abs(got - OS.decode_ref(batch, st))) < TOL[kv]
+    kr, vr = paged.pack_kv(st.kc, st.vc, st.tables, batch.total_lens)
+    assert np.array_equal(bits(k, kv), oracle_bits(kr, kv)) and np.array_equal(bits(v, kv), oracle_bits(vr, kv))
+
+
 def test_decode_repeated_calls_reuse_the_workspace():
     """Calls of different shapes and partition sizes, interleaved on one
     workspace, repeat bit-identically, and every call leaves the per-item
