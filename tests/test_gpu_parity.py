@@ -318,6 +318,44 @@ def test_every_compiled_decode_shape(kv, d, B, G):
     assert np.array_equal(bits(k, kv), oracle_bits(kr, kv)) and np.array_equal(bits(v, kv), oracle_bits(vr, kv))
 
 
+def test_step_replays_in_a_hip_graph():
+    """A decode step (store of the step's tokens, then pa_decode with a
+    caller-owned workspace) captured in a HIP graph: no call allocates or
+    synchronises, so it captures, and every replay, with eager work and
+    synchronisation between replays, gives the eager result bit for bit."""
+    from paged_kv_attention_26_amd import binding as pa, runner
+    say("[gpu] decode step in a HIP graph")
+    batch = W.config2(small=True)
+    g = runner.prepare(batch)
+    ws = pa.decode_workspace(1, 1, batch.head_dim, 1, 0)
+    out = torch.empty_like(g.dec["q"])
+
+    def step():
+        runner.store_step(g)
+        runner.decode_step(g, out=out, workspace=ws)
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                      # warm-up on the capture stream
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(4):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
+        other = runner.decode_step(g, partition_tokens=128)          # eager work between replays
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws[:4096 * 4])) == 0
+        del other
+
+
 def test_decode_repeated_calls_reuse_the_workspace():
     """Calls of different shapes and partition sizes, interleaved on one
     workspace, repeat bit-identically, and every call leaves the per-item
