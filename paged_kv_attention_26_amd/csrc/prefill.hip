@@ -14,9 +14,11 @@
 //    tiles of fewer heads).  The workgroup stages each 32-key K / V^T tile
 //    once into LDS, swizzled so that the MFMA operand reads are free of bank
 //    conflicts.  A bf16 cache is loaded straight into LDS (16-byte loads to
-//    LDS, no registers) through a ring of three buffers, two tiles ahead of
-//    their MFMAs; an fp8 cache is loaded into registers, converted to bf16
-//    and written to two buffers.  One barrier per tile.  Block ids come
+//    LDS, no registers) through a ring of four buffers, and each wave issues
+//    the next tile's S^T MFMAs among this tile's exponentials (the matrix
+//    cores then work under the wave's own softmax); an fp8 cache is loaded
+//    into registers, converted to bf16 and written to two buffers.  One
+//    barrier per tile.  Block ids come
 //    through the scalar cache.  Two workgroups share each CU, so the two waves on a
 //    SIMD belong to different workgroups and do not pass their barriers
 //    together: one's softmax can overlap the other's MFMAs.
@@ -70,7 +72,7 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
   constexpr int KBUF = KT * KROW;
   constexpr int BUF = KBUF + D * VROW;
   // A bf16 cache is staged straight from memory into LDS (16-byte loads to
-  // LDS) through a ring of three unpadded buffers; an fp8 cache goes through
+  // LDS) through a ring of four unpadded buffers; an fp8 cache goes through
   // registers, converted to bf16, into two padded buffers.
   constexpr bool DIRECT = KV == KV_BF16;
   constexpr int RBUF = KBUF + D * KT * 2;                  // ring buffer: K tile, then V^T tile
@@ -78,6 +80,7 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
   __shared__ __attribute__((aligned(16))) char ring0[DIRECT ? RBUF : 16];
   __shared__ __attribute__((aligned(16))) char ring1[DIRECT ? RBUF : 16];
   __shared__ __attribute__((aligned(16))) char ring2[DIRECT ? RBUF : 16];
+  __shared__ __attribute__((aligned(16))) char ring3[DIRECT ? RBUF : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -262,22 +265,25 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
   // before its own MFMAs and written to LDS one tile before them, so about
   // two tiles of MFMA work cover each load's latency.  Tiles past the last
   // re-read the last one.
-  auto compute_tile = [&](int kt, const char* sb) __attribute__((always_inline)) {
-    if (kt < n_tiles) {
+  // A tile in three parts.  qk_tile: S^T = K Q^T (A: lane row n = key
+  // k0 + my_key, dims 16s + 8hh).  mask_rescale: causal and end masks, the
+  // tile maximum and the lazy rescale.  probs_pv: probabilities and
+  // O^T += V^T P^T.  In the bf16 ring, probs_pv also issues the next tile's
+  // qk_tile among its exponentials, and every wave runs every tile of its
+  // workgroup: a tile past a wave's own keys is masked whole (probabilities
+  // 0, V rows zeroed), which leaves its results bit for bit as they were.
+  auto qk_tile = [&](const char* sb) __attribute__((always_inline)) -> f32x16_t {
+    uint4 ka[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      ka[s] = *reinterpret_cast<const uint4*>(sb + my_key * KROW + ((2 * s + hh) ^ kswz(my_key)) * 16);
+    f32x16_t sc = f32x16_t{};
+#pragma unroll
+    for (int st = 0; st < 8; ++st) sc = mfma32(ka[st], qb[st], sc);
+    return sc;
+  };
+  auto mask_rescale = [&](int kt, f32x16_t& sc) __attribute__((always_inline)) {
       const int k0 = kt * KT;
-      // ---- S^T = K Q^T  (A: lane row n = key k0 + my_key, dims 16s + 8hh)
-      uint4 ka[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        ka[s] = *reinterpret_cast<const uint4*>(sb + my_key * KROW + ((2 * s + hh) ^ kswz(my_key)) * 16);
-      f32x16_t sc = f32x16_t{};
-#pragma unroll
-      for (int st = 0; st < 8; ++st) sc = mfma32(ka[st], qb[st], sc);
-      // all eight operand reads go out before the first MFMA: one wait
-      // instead of one per pair
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-
       // accumulator r = 4i + j holds MFMA row 8i + 4hh + j, i.e. key k0 + swap23(8i + 4hh + j)
       if (k0 + KT - 1 > first_row_pos) {                 // tile reaches the diagonal or the end
 #pragma unroll
@@ -306,6 +312,11 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
           for (int r = 0; r < 16; ++r) o[dt][r] *= al;
         m_run = m_new;
       }
+  };
+  auto probs_pv = [&](int kt, const f32x16_t& sc, const char* sb, f32x16_t& s_next, const char* nsb,
+                      bool do_next) __attribute__((always_inline)) {
+      const int k0 = kt * KT;
+      if (do_next) s_next = qk_tile(nsb);
       const float mc = m_run * c;
       float p[16];
 #pragma unroll
@@ -319,6 +330,17 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
       for (int ks = 0; ks < 2; ++ks)
         pb[ks] = make_uint4(pack_bf16x2(p[8 * ks + 0], p[8 * ks + 1]), pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]),
                             pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]), pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7]));
+      if (do_next) {
+        // the next tile's eight K operand reads first, then each of its
+        // eight S^T MFMAs followed by six vector instructions of this tile,
+        // so that the matrix cores work under this wave's own softmax
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
+        }
+      }
       // V^T operands: d-tile dt (dims 32dt + n), key slice ks (keys k0 + 16ks + 8hh .. + 7)
       uint4 va[4][2];
 #pragma unroll
@@ -346,21 +368,31 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
         o[dt] = mfma32(va[dt][0], pb[0], o[dt]);
         o[dt] = mfma32(va[dt][1], pb[1], o[dt]);
       }
+  };
+  auto compute_tile = [&](int kt, const char* sb) __attribute__((always_inline)) {   // one tile, alone
+    if (kt < n_tiles) {
+      f32x16_t sc = qk_tile(sb);
+      mask_rescale(kt, sc);
+      f32x16_t unused;
+      probs_pv(kt, sc, sb, unused, sb, false);
     }
   };
 
   const int last = n_tiles_wg - 1;
   int j0, j1;
   if constexpr (DIRECT) {
-    // Ring of three buffers.  Tile kt + 2 is loaded into the buffer that
-    // held tile kt - 1, which every wave finished reading before the barrier
-    // that closed tile kt - 1.  A thread has four loads per tile, so once
-    // only its four newest are in flight (vmcnt(4)), its part of tile kt + 1
-    // is in LDS, and after the barrier all of it is.  The barrier is a plain
-    // s_barrier between compiler-only fences: a __syncthreads() would also
-    // wait for tile kt + 2.  Each buffer is a distinct array named
-    // statically, so the compiler does not take loads into one for writes to
-    // the one being read (it would wait for them before every LDS read).
+    // Ring of four buffers.  Step kt processes tile kt (its S^T was issued
+    // one step earlier) and issues tile kt + 1's S^T, so tile kt + 1 must be
+    // in LDS when step kt starts, and tile kt + 3 is requested into the
+    // buffer that held tile kt - 1, which every wave finished reading before
+    // the barrier that opens step kt.  A thread has four loads per tile, so
+    // once only its four newest (tile kt + 2) are in flight (vmcnt(4)), its
+    // part of tile kt + 1 is in LDS, and after the barrier all of it is.  The
+    // barrier is a plain s_barrier between compiler-only fences: a
+    // __syncthreads() would also wait for tile kt + 2.  Each buffer is a
+    // distinct array named statically, so the compiler does not take loads
+    // into one for writes to the one being read (it would wait for them
+    // before every LDS read).
 #define PA_RING_SYNC()                                                                                 \
     __builtin_amdgcn_s_waitcnt(0x0F74); /* vmcnt(4) */                                                 \
     __atomic_signal_fence(__ATOMIC_SEQ_CST);                                                           \
@@ -371,19 +403,29 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
     tile_ids(min(1, last), j0, j1);
     direct_stage(ring1, j0, j1);
     tile_ids(min(2, last), j0, j1);
-    __builtin_amdgcn_s_waitcnt(0x0F74);                     // vmcnt(4): tile 0 is in LDS
+    direct_stage(ring2, j0, j1);
+    tile_ids(min(3, last), j0, j1);
+    __builtin_amdgcn_s_waitcnt(0x0F78);                     // vmcnt(8): tile 0 is in LDS
     __syncthreads();                                          // (once: also settles the query loads)
-#define PA_RING_STEP(KT_, NEXT, CUR)                                                                   \
-    direct_stage(NEXT, j0, j1);                                                                        \
-    tile_ids(min((KT_) + 3, last), j0, j1);                                                            \
-    compute_tile((KT_), CUR);                                                                          \
-    PA_RING_SYNC()
-    for (int kt = 0; kt < n_tiles_wg; kt += 3) {
-      PA_RING_STEP(kt, ring2, ring0)
+    f32x16_t s_cur = qk_tile(ring0);
+#define PA_RING_STEP(KT_, CUR, NXT, LD)                                                                \
+    PA_RING_SYNC()                                                                                     \
+    direct_stage(LD, j0, j1);                                                                          \
+    tile_ids(min((KT_) + 4, last), j0, j1);                                                            \
+    {                                                                                                  \
+      f32x16_t s_nxt;                                                                                  \
+      mask_rescale((KT_), s_cur);                                                                      \
+      probs_pv((KT_), s_cur, CUR, s_nxt, NXT, true);                                                   \
+      s_cur = s_nxt;                                                                                   \
+    }
+    for (int kt = 0; kt < n_tiles_wg; kt += 4) {
+      PA_RING_STEP(kt, ring0, ring1, ring3)
       if (kt + 1 >= n_tiles_wg) break;
-      PA_RING_STEP(kt + 1, ring0, ring1)
+      PA_RING_STEP(kt + 1, ring1, ring2, ring0)
       if (kt + 2 >= n_tiles_wg) break;
-      PA_RING_STEP(kt + 2, ring1, ring2)
+      PA_RING_STEP(kt + 2, ring2, ring3, ring1)
+      if (kt + 3 >= n_tiles_wg) break;
+      PA_RING_STEP(kt + 3, ring3, ring0, ring2)
     }
 #undef PA_RING_STEP
 #undef PA_RING_SYNC
