@@ -17,8 +17,8 @@
 //    LDS, no registers) through a ring of four buffers, and each wave issues
 //    the next tile's S^T MFMAs among this tile's exponentials (the matrix
 //    cores then work under the wave's own softmax); an fp8 cache is loaded
-//    into registers, converted to bf16 and written to two buffers.  One
-//    barrier per tile.  Block ids come
+//    into registers, converted to bf16 and written to a ring of three
+//    buffers, with the same interleave.  One barrier per tile.  Block ids come
 //    through the scalar cache.  Two workgroups share each CU, so the two waves on a
 //    SIMD belong to different workgroups and do not pass their barriers
 //    together: one's softmax can overlap the other's MFMAs.
@@ -73,10 +73,10 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
   constexpr int BUF = KBUF + D * VROW;
   // A bf16 cache is staged straight from memory into LDS (16-byte loads to
   // LDS) through a ring of four unpadded buffers; an fp8 cache goes through
-  // registers, converted to bf16, into two padded buffers.
+  // registers, converted to bf16, into a ring of three padded buffers.
   constexpr bool DIRECT = KV == KV_BF16;
   constexpr int RBUF = KBUF + D * KT * 2;                  // ring buffer: K tile, then V^T tile
-  __shared__ __attribute__((aligned(16))) char smem[2][DIRECT ? 16 : BUF];   // double-buffered (fp8)
+  __shared__ __attribute__((aligned(16))) char smem[3][DIRECT ? 16 : BUF];   // ring of three (fp8)
   __shared__ __attribute__((aligned(16))) char ring0[DIRECT ? RBUF : 16];
   __shared__ __attribute__((aligned(16))) char ring1[DIRECT ? RBUF : 16];
   __shared__ __attribute__((aligned(16))) char ring2[DIRECT ? RBUF : 16];
@@ -268,10 +268,10 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
   // A tile in three parts.  qk_tile: S^T = K Q^T (A: lane row n = key
   // k0 + my_key, dims 16s + 8hh).  mask_rescale: causal and end masks, the
   // tile maximum and the lazy rescale.  probs_pv: probabilities and
-  // O^T += V^T P^T.  In the bf16 ring, probs_pv also issues the next tile's
-  // qk_tile among its exponentials, and every wave runs every tile of its
-  // workgroup: a tile past a wave's own keys is masked whole (probabilities
-  // 0, V rows zeroed), which leaves its results bit for bit as they were.
+  // O^T += V^T P^T, with the next tile's qk_tile issued among its
+  // exponentials.  Every wave runs every tile of its workgroup: a tile past
+  // a wave's own keys is masked whole (probabilities 0, V rows zeroed),
+  // which leaves its results bit for bit as they would be without it.
   auto qk_tile = [&](const char* sb) __attribute__((always_inline)) -> f32x16_t {
     uint4 ka[8];
 #pragma unroll
@@ -369,15 +369,6 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
         o[dt] = mfma32(va[dt][1], pb[1], o[dt]);
       }
   };
-  auto compute_tile = [&](int kt, const char* sb) __attribute__((always_inline)) {   // one tile, alone
-    if (kt < n_tiles) {
-      f32x16_t sc = qk_tile(sb);
-      mask_rescale(kt, sc);
-      f32x16_t unused;
-      probs_pv(kt, sc, sb, unused, sb, false);
-    }
-  };
-
   const int last = n_tiles_wg - 1;
   int j0, j1;
   if constexpr (DIRECT) {
@@ -431,27 +422,48 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
 #undef PA_RING_SYNC
     __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0): no load into LDS outlives the loop
   } else {
+  // Ring of three buffers filled through registers (fp8 codes converted to
+  // bf16 on the way): step kt computes tile kt + 1's S^T among tile kt's
+  // exponentials, then writes tile kt + 2 (loaded one step earlier) into the
+  // buffer that held tile kt - 1, and requests tile kt + 3 into the register
+  // set that tile kt + 2 leaves.
   typename Raw::T sa_k0{}, sa_v0{}, sb_k0{}, sb_v0{}, sa_k1{}, sa_v1{}, sb_k1{}, sb_v1{};
   tile_ids(0, j0, j1);
   PA_STAGE_LOAD(sa_, 0, j0, j1);
   tile_ids(min(1, last), j0, j1);
   PA_STAGE_LOAD(sb_, min(1, last), j0, j1);
   tile_ids(min(2, last), j0, j1);
-  PA_STAGE_STORE(sa_, 0);
+  PA_STAGE_STORE(sa_, 0);                                    // tile 0
+  PA_STAGE_LOAD(sa_, min(2, last), j0, j1);
+  tile_ids(min(3, last), j0, j1);
+  PA_STAGE_STORE(sb_, 1);                                    // tile 1
   __syncthreads();
-  for (int kt = 0; kt < n_tiles_wg; kt += 2) {
-    PA_STAGE_LOAD(sa_, min(kt + 2, last), j0, j1);          // tile kt + 2, stored at the odd half
-    tile_ids(min(kt + 3, last), j0, j1);
-    compute_tile(kt, smem[0]);
-    PA_STAGE_STORE(sb_, 1);                                  // tile kt + 1
-    __syncthreads();
+  f32x16_t s_cur = qk_tile(smem[0]);
+#define PA_FP8_STEP(KT_, LD, ST, CUR, NXT, SBUF)                                                       \
+  PA_STAGE_LOAD(LD, 0, j0, j1);                              /* tile KT_ + 3 */                        \
+  tile_ids(min((KT_) + 4, last), j0, j1);                                                             \
+  {                                                                                                   \
+    f32x16_t s_nxt;                                                                                   \
+    mask_rescale((KT_), s_cur);                                                                       \
+    probs_pv((KT_), s_cur, CUR, s_nxt, NXT, true);                                                    \
+    s_cur = s_nxt;                                                                                    \
+  }                                                                                                   \
+  PA_STAGE_STORE(ST, SBUF);                                  /* tile KT_ + 2 */                        \
+  __syncthreads();
+  for (int kt = 0; kt < n_tiles_wg; kt += 6) {
+    PA_FP8_STEP(kt, sb_, sa_, smem[0], smem[1], 2)
     if (kt + 1 >= n_tiles_wg) break;
-    PA_STAGE_LOAD(sb_, min(kt + 3, last), j0, j1);          // tile kt + 3, stored at the next even half
-    tile_ids(min(kt + 4, last), j0, j1);
-    compute_tile(kt + 1, smem[1]);
-    PA_STAGE_STORE(sa_, 0);                                  // tile kt + 2
-    __syncthreads();
+    PA_FP8_STEP(kt + 1, sa_, sb_, smem[1], smem[2], 0)
+    if (kt + 2 >= n_tiles_wg) break;
+    PA_FP8_STEP(kt + 2, sb_, sa_, smem[2], smem[0], 1)
+    if (kt + 3 >= n_tiles_wg) break;
+    PA_FP8_STEP(kt + 3, sa_, sb_, smem[0], smem[1], 2)
+    if (kt + 4 >= n_tiles_wg) break;
+    PA_FP8_STEP(kt + 4, sb_, sa_, smem[1], smem[2], 0)
+    if (kt + 5 >= n_tiles_wg) break;
+    PA_FP8_STEP(kt + 5, sa_, sb_, smem[2], smem[0], 1)
   }
+#undef PA_FP8_STEP
   }
 #undef PA_STAGE_LOAD
 #undef PA_STAGE_STORE
