@@ -50,7 +50,8 @@ enum {
   PA_ERR_UNSUPPORTED = -4, /* head_dim / block_size / group size not compiled   */
   PA_ERR_WORKSPACE = -5,   /* workspace smaller than pa_decode_workspace_bytes() */
   PA_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed         */
-  PA_ERR_NO_BLOCKS = -7    /* block manager: the pool has no free block          */
+  PA_ERR_NO_BLOCKS = -7,   /* block manager: the pool has no free block          */
+  PA_ERR_PENDING = -8      /* block manager: copy pairs are queued (take them)   */
 };
 
 /* A paged KV cache (the pools are device memory owned by the caller).
@@ -230,6 +231,14 @@ const char* pa_last_error(void);
  *    a new block; otherwise a shared tail block (reference count > 1) is
  *    first copied: a new block is taken, the pair (old, new) is queued for
  *    pa_copy_blocks and the old block loses one reference.
+ *  - ORDER: a queued pair is a copy that has not run.  pa_bm_fork and
+ *    pa_bm_release fail with PA_ERR_PENDING while pairs are queued (a fork
+ *    then could make a queued pair's dst shared again, so that the next
+ *    append queues a copy out of it -- a chain pa_copy_blocks cannot run --
+ *    and a release could free a queued pair's block and hand it out again).
+ *    Take the pairs with pa_bm_take_copies, and on the stream run
+ *    pa_copy_blocks with them and then pa_store_kv of the slots handed out
+ *    so far, before the copies and stores of later appends.
  * All ids are int32; functions returning int return PA_ERR_* on failure.
  * Not thread-safe: one manager per thread. */
 typedef struct pa_block_manager pa_block_manager;

@@ -20,6 +20,16 @@ and section 2.3 (手写一个 Block Manager):
   block on write first;
 * ``fork`` shares every block of the parent (one more reference each).
 
+Copies must not chain.  Every recorded (src, dst) pair is a copy that has not
+run yet, and the block-copy call runs a batch of pairs concurrently.  Forking
+while pairs are queued could make the tail block a queued copy's dst shared
+again.  The next append would then queue a copy *from* that dst (a chain),
+and the parent's freshly stored token would be copied before it lands.
+Releasing while pairs are queued can free a queued pair's block and hand it
+out again.  So ``fork`` and ``release`` refuse (RuntimeError) while pairs
+are queued: the caller takes them, runs them and the stores of the slots
+handed out so far, and then forks or releases.
+
 Unlike the page's version, blocks hold no token lists: the data lives in the
 device cache, so ``cow`` records the (src, dst) pair that a block-copy call
 must carry out, and ``append_slot`` returns the slot (physical block *
@@ -116,6 +126,8 @@ class Sequence:
         return [self.append_slot() for _ in range(n)]
 
     def fork(self, new_id: int) -> "Sequence":
+        if self.mgr.pending_copies:
+            raise RuntimeError("fork while copy pairs are queued: take and run them first")
         child = Sequence(self.mgr, new_id)
         child.block_table = list(self.block_table)
         child.length = self.length
@@ -124,6 +136,8 @@ class Sequence:
         return child
 
     def release(self) -> None:
+        if self.mgr.pending_copies:
+            raise RuntimeError("release while copy pairs are queued: take and run them first")
         for bid in self.block_table:
             self.mgr.free(bid)
         self.block_table = []

@@ -12,12 +12,12 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, \
-    PA_ERR_NO_BLOCKS = 0, -1, -2, -3, -4, -5, -6, -7
+    PA_ERR_NO_BLOCKS, PA_ERR_PENDING = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 ERROR_NAMES = {
     PA_ERR_NULL: "PA_ERR_NULL", PA_ERR_SHAPE: "PA_ERR_SHAPE", PA_ERR_DTYPE: "PA_ERR_DTYPE",
     PA_ERR_UNSUPPORTED: "PA_ERR_UNSUPPORTED", PA_ERR_WORKSPACE: "PA_ERR_WORKSPACE", PA_ERR_HIP: "PA_ERR_HIP",
-    PA_ERR_NO_BLOCKS: "PA_ERR_NO_BLOCKS",
+    PA_ERR_NO_BLOCKS: "PA_ERR_NO_BLOCKS", PA_ERR_PENDING: "PA_ERR_PENDING",
 }
 
 

@@ -55,6 +55,7 @@ struct pa_block_manager {
     return n;
   }
   bool valid_seq(int32_t s) const { return s >= 0 && size_t(s) < seqs.size(); }
+  size_t queued_copies() const { return (copies.size() - copies_head) / 2; }
 
   // ---- prefix cache --------------------------------------------------------
   // A node is one interned chain key.  It stays interned while its block is
@@ -237,6 +238,8 @@ int32_t pa_bm_append(pa_block_manager* bm, int32_t seq, int32_t n, int32_t* slot
 int32_t pa_bm_fork(pa_block_manager* bm, int32_t seq) {
   if (!bm) return bm_fail(PA_ERR_NULL, "block manager is NULL");
   if (!bm->valid_seq(seq)) return bm_fail(PA_ERR_SHAPE, "unknown sequence %d", seq);
+  if (bm->queued_copies())
+    return bm_fail(PA_ERR_PENDING, "fork of sequence %d while %zu copy pairs are queued", seq, bm->queued_copies());
   pa_block_manager::Seq child = bm->seqs[size_t(seq)];
   for (int32_t b : child.table) bm->ref[size_t(b)] += 1;
   bm->seqs.push_back(std::move(child));
@@ -246,6 +249,9 @@ int32_t pa_bm_fork(pa_block_manager* bm, int32_t seq) {
 int pa_bm_release(pa_block_manager* bm, int32_t seq) {
   if (!bm) return bm_fail(PA_ERR_NULL, "block manager is NULL");
   if (!bm->valid_seq(seq)) return bm_fail(PA_ERR_SHAPE, "unknown sequence %d", seq);
+  if (bm->queued_copies())
+    return bm_fail(PA_ERR_PENDING, "release of sequence %d while %zu copy pairs are queued", seq,
+                   bm->queued_copies());
   auto& s = bm->seqs[size_t(seq)];
   for (int32_t b : s.table) bm->release_block(b);
   s.table.clear();

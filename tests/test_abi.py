@@ -213,6 +213,36 @@ def test_native_block_manager_fork_demo():
     assert len(pairs) == 4 and len(set(pairs[:, 0].tolist())) == 1
 
 
+def test_native_block_manager_refuses_fork_and_release_while_copies_are_queued():
+    """Append, fork, append without taking the first copy pair would chain
+    copies (the second pair reads the first pair's destination): both
+    managers refuse the fork, and the release, until the pairs are taken,
+    and then take the same decisions."""
+    o = OracleBM(16, 4, list(range(16)))
+    n = NativeBM(16, 4, list(range(16)))
+    oa, na = OracleSeq(o, 0), n.seq_new()
+    assert oa.append_slots(2) == n.append(na, 2).tolist()
+    ob, nb = oa.fork(1), n.fork(na)
+    assert [oa.append_slot()] == n.append(na, 1).tolist()      # CoW of the shared tail
+    with pytest.raises(RuntimeError):
+        oa.fork(2)
+    with pytest.raises(L.PaError) as e:
+        n.fork(na)
+    assert e.value.code == L.PA_ERR_PENDING
+    with pytest.raises(RuntimeError):
+        ob.release()
+    with pytest.raises(L.PaError) as e:
+        n.release(nb)
+    assert e.value.code == L.PA_ERR_PENDING
+    assert n.take_copies().tolist() == [list(p) for p in o.take_copies()]
+    oc, nc = oa.fork(2), n.fork(na)
+    assert [oa.append_slot()] == n.append(na, 1).tolist()
+    got, want = n.take_copies().tolist(), [list(p) for p in o.take_copies()]
+    assert got == want and len(got) == 1
+    ob.release(), n.release(nb)
+    assert [n.ref_count(b) for b in range(16)] == o.ref_count
+
+
 def test_native_block_manager_rejects_bad_free_order():
     with pytest.raises(L.PaError):
         NativeBM(4, 16, [0, 1, 1, 3])

@@ -56,6 +56,33 @@ def test_exhaustion_returns_none_and_cow_raises():
         Sequence(mgr, 2).append_slot()
 
 
+def test_fork_and_release_refuse_while_copies_are_queued():
+    """Append (a CoW of a shared tail), fork, append again: with the first
+    pair still queued, the second append would copy out of the first pair's
+    destination (a chain), and the parent's new token would be copied before
+    it is stored.  Fork and release refuse until the pairs are taken; after
+    that the same trace queues one plain pair per step."""
+    mgr = BlockManager(16, 4)
+    a = Sequence(mgr, 0)
+    a.append_slots(2)
+    b = a.fork(1)                         # tail (2 tokens) shared, count 2
+    a.append_slot()                       # CoW: a takes a copy of the tail
+    assert len(mgr.pending_copies) == 1
+    with pytest.raises(RuntimeError):
+        a.fork(2)
+    with pytest.raises(RuntimeError):
+        b.release()
+    (src, dst), = mgr.take_copies()
+    c = a.fork(2)                         # a's new tail (dst) is shared now
+    assert mgr.ref_count[dst] == 2
+    a.append_slot()                       # a copies dst on write: one pair, no chain
+    (src2, dst2), = mgr.take_copies()
+    assert src2 == dst and dst2 not in (src, dst)
+    assert c.block_table[-1] == dst and a.block_table[-1] == dst2
+    b.release()
+    assert mgr.ref_count[src] == 0
+
+
 def test_free_list_order_and_release():
     mgr = BlockManager(5, 4, free_order=[3, 1, 4, 0, 2])
     s = Sequence(mgr, 0)
