@@ -133,8 +133,9 @@ int pa_pack_kv(const pa_kv_cache* cache, const int32_t* block_table, int32_t max
 
 /* Bytes of device workspace pa_decode needs (host call, no HIP): two partial
  * results per wavefront for at most 4096 wavefronts and 8 query heads per kv
- * head, about 34 MB at head_dim 128 whatever the batch.  partition_tokens as
- * for pa_decode.  Returns 0 for invalid sizes. */
+ * head, about 34 MB at head_dim 128 whatever the batch (one size serves
+ * every shape, so one buffer serves every call on a stream).  Returns 0 for
+ * negative sizes. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_tokens);
 
@@ -154,12 +155,14 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   (the softmax scale, 1/sqrt(head_dim) for the pages' attention).
  *
  * Work is cut into partitions of partition_tokens tokens of one (sequence,
- * kv head) (0 = 64; otherwise a multiple of 64 and at most 64 * block_size).
- * Every wavefront of the launch takes an equal, contiguous run of
- * partitions and keeps a running max / sum across the partitions of one
- * (sequence, kv head); where runs cut a (sequence, kv head) apart, their
- * partial results are merged by log-sum-exp rescaling, in the same kernel,
- * by whichever of those wavefronts finishes last.
+ * kv head): a positive multiple of block_size (64 is the fastest on
+ * MI355X), or 0 for no split (one partition spans max_context_len, so no
+ * (sequence, kv head) is shared between wavefronts).  Every wavefront of the
+ * launch takes an equal, contiguous run of partitions and keeps a running
+ * max / sum across the partitions of one (sequence, kv head); where runs cut
+ * a (sequence, kv head) apart, their partial results are merged by
+ * log-sum-exp rescaling, in the same kernel, by whichever of those
+ * wavefronts finishes last.
  * The result does not depend on partition_tokens or on the split beyond
  * fp32 rounding.
  *

@@ -157,8 +157,10 @@ def _default_workspace(head_dim, device, stream_handle) -> torch.Tensor:
 
 
 def decode(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor, context_lens: torch.Tensor,
-           max_context_len: int, scale: float, out: Optional[torch.Tensor] = None, partition_tokens: int = 0,
+           max_context_len: int, scale: float, out: Optional[torch.Tensor] = None, partition_tokens: int = 64,
            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pa_decode.  partition_tokens: a multiple of the block size (64, the
+    default, is the fastest split), or 0 for no split."""
     S, Hq, D = q.shape
     if D != cache.head_dim:
         raise ValueError("q head_dim does not match the cache")

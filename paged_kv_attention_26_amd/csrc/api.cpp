@@ -35,7 +35,8 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr int kDefaultPartition = 64;
+// Largest partition: unit counts and token offsets stay far inside int32.
+constexpr int32_t kMaxPartition = 1 << 28;
 constexpr int kMaxSeqs = 8192;  // the decode kernel keeps a prefix over sequences in LDS
 
 int elem_bytes(int dt) { return dt == PA_F32 ? 4 : dt == PA_BF16 ? 2 : 1; }
@@ -60,12 +61,19 @@ int check_cache(const pa_kv_cache* c) {
 
 int io_dtype_for(int cache_dtype) { return cache_dtype == PA_F32 ? PA_F32 : PA_BF16; }
 
-int resolve_partition(int32_t p, int32_t block_size, int32_t* out) {
-  if (p == 0) p = kDefaultPartition;
-  if (p < 64 || p % 64 != 0) return fail(PA_ERR_SHAPE, "partition_tokens %d must be a positive multiple of 64", p);
-  if (p % block_size != 0 || p > 64 * block_size)
+// partition_tokens 0: no split -- one partition spans the longest context,
+// so every (sequence, kv head) is one unit and no wave shares one.
+// Otherwise a positive multiple of block_size.
+int resolve_partition(int32_t p, int32_t block_size, int32_t max_context_len, int32_t* out) {
+  if (p < 0) return fail(PA_ERR_SHAPE, "partition_tokens %d < 0", p);
+  if (p == 0) {
+    const int64_t whole = (int64_t(max_context_len > 0 ? max_context_len : 1) + 63) / 64 * 64;
+    *out = int32_t(whole < kMaxPartition ? whole : kMaxPartition);
+    return PA_OK;
+  }
+  if (p % block_size != 0 || p > kMaxPartition)
     return fail(PA_ERR_SHAPE, "partition_tokens %d must be a multiple of block_size %d and at most %d", p,
-                block_size, 64 * block_size);
+                block_size, kMaxPartition);
   *out = p;
   return PA_OK;
 }
@@ -172,9 +180,7 @@ int pa_pack_kv(const pa_kv_cache* cache, const int32_t* block_table, int32_t max
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_tokens) {
-  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
-  int32_t P = partition_tokens == 0 ? kDefaultPartition : partition_tokens;
-  if (P < 64 || P % 64) return 0;
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 || partition_tokens < 0) return 0;
   return pa::decode_workspace_layout(head_dim).total;
 }
 
@@ -202,7 +208,7 @@ int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* ou
                 (long long)need_blocks);
   if (!(std::isfinite(scale)) || !(scale > 0.f)) return fail(PA_ERR_SHAPE, "scale must be finite and > 0");
   int32_t P = 0;
-  rc = resolve_partition(partition_tokens, cache->block_size, &P);
+  rc = resolve_partition(partition_tokens, cache->block_size, max_context_len, &P);
   if (rc) return rc;
   if (num_seqs == 0) return PA_OK;
   if (!q || !out || !block_table || !context_lens || !workspace)

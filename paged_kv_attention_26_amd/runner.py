@@ -108,7 +108,7 @@ def store_step(g: GpuBatch) -> None:
         pa.store_kv(g.cache, g.k_step, g.v_step, g.step_slots)
 
 
-def decode_step(g: GpuBatch, out=None, partition_tokens=0, workspace=None) -> torch.Tensor:
+def decode_step(g: GpuBatch, out=None, partition_tokens=64, workspace=None) -> torch.Tensor:
     d = g.dec
     return pa.decode(g.cache, d["q"], d["table"], d["lens"], d["max_len"], g.batch.scale, out=out,
                      partition_tokens=partition_tokens, workspace=workspace)
@@ -188,7 +188,7 @@ def run_fork(fb, device="cuda", snapshot=None) -> GpuFork:
                    np.stack(slots_all))
 
 
-def fork_decode(gf: GpuFork, device="cuda", out=None, partition_tokens=0, workspace=None) -> torch.Tensor:
+def fork_decode(gf: GpuFork, device="cuda", out=None, partition_tokens=64, workspace=None) -> torch.Tensor:
     bm = gf.bm
     table = _t(bm.block_tables(gf.beams, gf.pad), device)
     lens = np.array([bm.seq_len(b) for b in gf.beams], dtype=np.int32)
@@ -253,3 +253,60 @@ def run_prefix_agent(w, device="cuda"):
             bm.release(s)
         turns.append(PrefixTurn(active, hits, tables, out_p, out_d))
     return cache, bm, turns
+
+
+@dataclass
+class SpecBranchRun:
+    cache: pa.KVCache
+    bm: pa.BlockManager
+    copy_pairs: np.ndarray
+    branch_tables: list
+    target_tables: list
+    verify_out: torch.Tensor
+    decode_out: torch.Tensor
+
+
+def run_spec_branch(w, device="cuda") -> SpecBranchRun:
+    """Speculative decoding over copy-on-write branches through libpa: store
+    the targets' prefixes, fork one draft branch per target, append the
+    drafts to the branches (their first append copies the shared tail: the
+    queued pairs go to pa_copy_blocks before the drafts' pa_store_kv), verify
+    the drafts with pa_prefill_chunk over the branches, append the accepted
+    drafts to the targets and store them, release the branches, and decode
+    the targets' next token."""
+    bm = pa.BlockManager(w.num_blocks, w.block_size, w.free_order)
+    S = len(w.prefix_lens)
+    cache = pa.alloc_cache(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, w.kv_dtype,
+                           device=device, k_scale=w.k_scale, v_scale=w.v_scale)
+    targets = [bm.seq_new() for _ in range(S)]
+    slots = [bm.append(t, int(n)) for t, n in zip(targets, w.prefix_lens)]
+    pa.store_kv(cache, _t(w.k_prefix, device), _t(w.v_prefix, device),
+                _t(np.concatenate(slots).astype(np.int32), device))
+    branches = [bm.fork(t) for t in targets]
+    dslots = [bm.append(b, w.draft) for b in branches]
+    pairs = bm.take_copies()
+    if len(pairs):
+        pa.copy_blocks(cache, _t(pairs.astype(np.int32), device))
+    Hkv, d = w.num_kv_heads, w.head_dim
+    pa.store_kv(cache, _t(w.k_draft.reshape(-1, Hkv, d), device), _t(w.v_draft.reshape(-1, Hkv, d), device),
+                _t(np.concatenate(dslots).astype(np.int32), device))
+    btables = [bm.block_table(b) for b in branches]
+    cu = (np.arange(S + 1) * w.draft).astype(np.int32)
+    lens = (w.prefix_lens + w.draft).astype(np.int32)
+    verify = pa.prefill_chunk(cache, _t(w.q_verify, device), _t(cu, device), _t(lens, device),
+                              _t(bm.block_tables(branches, bm.unused_block()), device), w.draft,
+                              int(lens.max()), w.scale).clone()
+    aslots = [bm.append(t, int(a)) for t, a in zip(targets, w.accepted)]
+    if len(bm.take_copies()):
+        raise RuntimeError("a target's tail was still shared after its branch copied it")
+    rows = [(i, j) for i in range(S) for j in range(int(w.accepted[i]))]
+    if rows:
+        ii, jj = np.array(rows).T
+        pa.store_kv(cache, _t(w.k_draft[ii, jj], device), _t(w.v_draft[ii, jj], device),
+                    _t(np.concatenate(aslots).astype(np.int32), device))
+    for b in branches:
+        bm.release(b)
+    ctx = (w.prefix_lens + w.accepted).astype(np.int32)
+    dec = pa.decode(cache, _t(w.q_next, device), _t(bm.block_tables(targets, bm.unused_block()), device),
+                    _t(ctx, device), int(ctx.max()), w.scale).clone()
+    return SpecBranchRun(cache, bm, pairs, btables, [bm.block_table(t) for t in targets], verify, dec)

@@ -194,3 +194,63 @@ def build_prefix_agent(w):
             s.release()
         turns.append(PrefixTurnRef(active, hits, tables, out_p, out_d))
     return kc, vc, mgr, cache, turns
+
+
+@dataclass
+class SpecBranchRef:
+    kc: np.ndarray
+    vc: np.ndarray
+    copy_pairs: list       # pairs the branches' first appends recorded
+    branch_tables: list    # branch block tables at verification
+    target_tables: list    # target block tables after the accepted tokens
+    ref_count: list
+    used_blocks: int
+    verify_out: np.ndarray
+    decode_out: np.ndarray
+
+
+def build_spec_branch(w) -> SpecBranchRef:
+    """The oracle's run of speculative decoding over copy-on-write branches
+    (nanoPD page, 分页KV缓存: copy on write serves speculative branches;
+    serving-stack page section 7: the target checks the k draft tokens in one
+    pass and keeps the accepted ones): store the targets' prefixes, fork a
+    branch per target, append the drafts to the branches (copy pairs run
+    before the drafts' store), verify over the branches, append the accepted
+    drafts to the targets, release the branches, decode the targets."""
+    mgr = BlockManager(w.num_blocks, w.block_size, w.free_order)
+    S = len(w.prefix_lens)
+    targets = [Sequence(mgr, i) for i in range(S)]
+    kc, vc = paged.new_pools(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, w.kv_dtype)
+    slots = [t.append_slots(int(n)) for t, n in zip(targets, w.prefix_lens)]
+    paged.store_kv(kc, vc, w.kv_dtype, w.k_prefix, w.v_prefix, w.io_dtype,
+                   np.concatenate(slots).astype(np.int64), w.k_scale, w.v_scale)
+    branches = [t.fork(100 + i) for i, t in enumerate(targets)]
+    dslots = [b.append_slots(w.draft) for b in branches]
+    pairs = mgr.take_copies()
+    paged.copy_blocks(kc, vc, pairs)
+    paged.store_kv(kc, vc, w.kv_dtype, w.k_draft.reshape(-1, w.num_kv_heads, w.head_dim),
+                   w.v_draft.reshape(-1, w.num_kv_heads, w.head_dim), w.io_dtype,
+                   np.concatenate(dslots).astype(np.int64), w.k_scale, w.v_scale)
+    held = {blk for s in targets + branches for blk in s.block_table}
+    pad = next(b for b in range(w.num_blocks) if b not in held)
+    cu = np.arange(S + 1, dtype=np.int64) * w.draft
+    btables = [list(b.block_table) for b in branches]
+    verify = paged.prefill_chunk_attention(kc, vc, w.kv_dtype, w.q_verify, w.io_dtype, cu,
+                                           w.prefix_lens + w.draft, table_array(btables, pad), w.scale,
+                                           w.k_scale, w.v_scale)
+    aslots = [t.append_slots(int(a)) for t, a in zip(targets, w.accepted)]
+    assert not mgr.take_copies()                 # the targets' tails are theirs alone now
+    rows = [(i, j) for i in range(S) for j in range(int(w.accepted[i]))]
+    if rows:
+        ii, jj = np.array(rows).T
+        paged.store_kv(kc, vc, w.kv_dtype, w.k_draft[ii, jj], w.v_draft[ii, jj], w.io_dtype,
+                       np.concatenate(aslots).astype(np.int64), w.k_scale, w.v_scale)
+    for b in branches:
+        b.release()
+    held = {blk for s in targets for blk in s.block_table}
+    pad = next(b for b in range(w.num_blocks) if b not in held)
+    ttables = [list(t.block_table) for t in targets]
+    dec = paged.decode_attention(kc, vc, w.kv_dtype, w.q_next, w.io_dtype, table_array(ttables, pad),
+                                 w.prefix_lens + w.accepted, w.scale, w.k_scale, w.v_scale)
+    return SpecBranchRef(kc, vc, [tuple(p) for p in pairs], btables, ttables, list(mgr.ref_count),
+                         mgr.used_blocks, verify, dec)

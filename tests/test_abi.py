@@ -67,8 +67,9 @@ def decode_call(c, **kw):
     (dict(c=cache(), q_dtype=L.PA_F32), L.PA_ERR_DTYPE),
     (dict(c=cache(dtype=L.PA_F32)), L.PA_ERR_DTYPE),                 # bf16 q on an f32 cache
     (dict(c=cache(), max_blocks=3), L.PA_ERR_SHAPE),                 # 64 tokens need 4 blocks
-    (dict(c=cache(), part=100), L.PA_ERR_SHAPE),
-    (dict(c=cache(), part=2048), L.PA_ERR_SHAPE),                    # > 64 blocks of 16
+    (dict(c=cache(), part=100), L.PA_ERR_SHAPE),                     # not a multiple of block_size
+    (dict(c=cache(), part=-16), L.PA_ERR_SHAPE),
+    (dict(c=cache(), part=(1 << 28) + 16), L.PA_ERR_SHAPE),          # beyond the largest partition
     (dict(c=cache(), ws_bytes=16), L.PA_ERR_WORKSPACE),
     (dict(c=cache(), lens=None), L.PA_ERR_NULL),
     (dict(c=cache(), S=-1), L.PA_ERR_SHAPE),
@@ -149,7 +150,7 @@ def test_workspace_size_query():
     assert a >= 4096 * 2 * 8 * (128 + 2) * 4
     assert lib.pa_decode_workspace_bytes(32, 32, 64, 4096, 512) < a
     assert lib.pa_decode_workspace_bytes(-1, 32, 128, 4096, 512) == 0
-    assert lib.pa_decode_workspace_bytes(32, 32, 128, 4096, 100) == 0
+    assert lib.pa_decode_workspace_bytes(32, 32, 128, 4096, -64) == 0
 
 
 # ------------------------------------------- native block manager == oracle

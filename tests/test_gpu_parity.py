@@ -192,11 +192,16 @@ def test_store_slot_patterns_bit_exact(kv, B, D, T):
 
 
 @pytest.mark.parametrize("name", list(SMALL))
-@pytest.mark.parametrize("part", [0, 64, 128, 512])
+@pytest.mark.parametrize("part", [0, 64, 128, 512, "B", "3B"])
 def test_decode_matches_oracle(name, part):
+    """Decode against the oracle at partitions of 64, 128 and 512 tokens,
+    one and three blocks (steps of 64 tokens then span several partitions,
+    and a wave's range can start inside a step) and 0 (no split)."""
     from paged_kv_attention_26_amd import runner
-    say(f"[gpu] decode {name} partition {part}")
     batch = SMALL[name]()
+    if isinstance(part, str):
+        part = batch.block_size * (3 if part == "3B" else 1)
+    say(f"[gpu] decode {name} partition {part}")
     g = runner.prepare(batch)
     runner.store_step(g)
     out = runner.decode_step(g, partition_tokens=part)
@@ -209,10 +214,10 @@ def test_decode_matches_oracle(name, part):
     assert err < TOL[batch.kv_dtype]
 
 
-@pytest.mark.parametrize("part", [0, 1024])
+@pytest.mark.parametrize("part", [64, 1024, 0])
 def test_decode_at_the_sequence_limit(part):
-    """The largest batch one call takes (8192 sequences), at the default and
-    at the largest partition (64 blocks of 16): store bit-exact over the
+    """The largest batch one call takes (8192 sequences), at the default
+    partition, at 64 blocks of 16 and with no split: store bit-exact over the
     whole pool, every output against the oracle, and the pack of every
     sequence bit-exact."""
     from oracle import paged
@@ -622,28 +627,41 @@ def test_prefill_chunk_of_one_row_matches_decode():
     assert np.max(np.abs(pre - dec)) < 1e-2
 
 
-def test_prefill_full_mixed_batch_sampled():
-    """The full mixed chunked-prefill batch (8 chunks of 512 on prefixes up to
-    7680, 64 decodes): every output of two chunk sequences against the oracle."""
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_prefill_full_mixed_batch(kv):
+    """The full mixed chunked-prefill batch as benchmarked (8 chunks of 512 on
+    prefixes up to 7680, 64 decodes beside them), bf16 and fp8 caches: every
+    output row of every chunk, and every decode output, against the oracle;
+    the 4160-row store of the step bit for bit over the whole pool."""
     from paged_kv_attention_26_amd import runner
-    say("[gpu] prefill full mixed batch")
-    batch = W.config4()
+    say(f"[gpu] prefill full mixed batch {kv}")
+    batch = W.config4(kv_dtype=kv)
     g = runner.prepare(batch)
     runner.store_step(g)
     out = out_f64(runner.chunk_step(g))
+    dec = out_f64(runner.decode_step(g))
     torch.cuda.synchronize()
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(dec))
     st = OS.build(batch)
+    assert np.array_equal(bits(g.cache.k_cache, kv), oracle_bits(st.kc, kv))
+    assert np.array_equal(bits(g.cache.v_cache, kv), oracle_bits(st.vc, kv))
+    del g
+    from oracle import paged
     ch = np.flatnonzero(batch.is_chunk)
     cu = np.concatenate([[0], np.cumsum(batch.new_lens[ch])])
-    from oracle import paged
-    for j in (0, len(ch) - 1):
-        i = ch[j]
+    worst = 0.0
+    for j, i in enumerate(ch):
         tab = OS.table_array([st.tables[i]], st.pad_block)
-        ref = paged.prefill_chunk_attention(st.kc, st.vc, "bf16", batch.q_chunk[cu[j]:cu[j + 1]], "bf16",
-                                            [0, int(batch.new_lens[i])], [int(batch.total_lens[i])], tab, batch.scale)
+        ref = paged.prefill_chunk_attention(st.kc, st.vc, kv, batch.q_chunk[cu[j]:cu[j + 1]], "bf16",
+                                            [0, int(batch.new_lens[i])], [int(batch.total_lens[i])], tab,
+                                            batch.scale, batch.k_scale, batch.v_scale)
         err = np.max(np.abs(out[cu[j]:cu[j + 1]] - ref))
-        say(f"      seq {j} (prefix {int(batch.prior_lens[i])}) max abs err {err:.3e}")
-        assert err < TOL["bf16"]
+        worst = max(worst, err)
+        say(f"      chunk {j} (prefix {int(batch.prior_lens[i])}) max abs err {err:.3e}")
+        assert err < TOL[kv]
+    derr = np.max(np.abs(dec - OS.decode_ref(batch, st)))
+    say(f"      all {len(ch)} chunks max abs err {worst:.3e}; {int((~batch.is_chunk).sum())} decodes {derr:.3e}")
+    assert derr < TOL[kv]
 
 
 # ------------------------------------------------ pack (KV hand-off)
@@ -661,6 +679,23 @@ def test_pack_is_bit_exact(name):
     wk, wv = paged.pack_kv(st.kc, st.vc, st.tables, batch.total_lens)
     assert np.array_equal(bits(k, batch.kv_dtype), oracle_bits(wk, batch.kv_dtype))
     assert np.array_equal(bits(v, batch.kv_dtype), oracle_bits(wv, batch.kv_dtype))
+
+
+def test_pack_full_qwen3_layer():
+    """The hand-off pack the bench times (the Qwen3-8B decode layer's 32
+    sequences, 72k tokens, 296 MB) bit for bit against the oracle's gather."""
+    from oracle import paged
+    from paged_kv_attention_26_amd import runner
+    say("[gpu] pack full qwen3-8b layer")
+    batch = W.config2()
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    k, v = runner.pack_all(g)
+    torch.cuda.synchronize()
+    st = OS.build(batch)
+    wk, wv = paged.pack_kv(st.kc, st.vc, st.tables, batch.total_lens)
+    assert np.array_equal(bits(k, "bf16"), wk) and np.array_equal(bits(v, "bf16"), wv)
+    say(f"      {k.shape[0]} rows bit-exact")
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
@@ -702,7 +737,7 @@ def test_decode_full_qwen3_layer():
     g = runner.prepare(batch)
     runner.store_step(g)
     ws = pa.decode_workspace(1, 1, batch.head_dim, 1, 0)
-    got = out_f64(runner.decode_step(g, partition_tokens=0, workspace=ws))
+    got = out_f64(runner.decode_step(g, partition_tokens=64, workspace=ws))
     torch.cuda.synchronize()
     err = np.max(np.abs(got - OS.decode_ref(batch, OS.build(batch))))
     say(f"      max abs err {err:.3e}")
@@ -722,12 +757,13 @@ def _long_context(B):
 
 
 @pytest.mark.parametrize("B", [16, 32])
-def test_decode_full_long_context_sampled(B):
+def test_decode_full_long_context(B):
     """Long-context decode at full size (128 seqs, 713k tokens, contexts up
-    to 28k) with 512-token partitions, as benchmarked: the longest, the
-    shortest and six seeded sequences against the oracle one by one.  The
-    bulk store that filled the pool (the bench's bulk-store case) is checked
-    bit for bit over the whole poisoned pool."""
+    to 28k) with 512-token partitions, as benchmarked: every sequence against
+    the oracle.  The bulk store that filled the pool (the bench's bulk-store
+    case) is checked bit for bit over the whole poisoned pool, and at block
+    16 so is the bench's bulk copy (every free block receives a copy of a
+    used one: 11 164 pairs of 64 KB per pool pair)."""
     from oracle import paged
     from paged_kv_attention_26_amd import binding as pa, runner
     say(f"[gpu] decode full long context B{B}")
@@ -737,21 +773,37 @@ def test_decode_full_long_context_sampled(B):
     ws = pa.decode_workspace(1, 1, batch.head_dim, 1, 512)
     got = out_f64(runner.decode_step(g, partition_tokens=512, workspace=ws))
     torch.cuda.synchronize()
+    assert np.all(np.isfinite(got))
     st = OS.build(batch)
     assert np.array_equal(bits(g.cache.k_cache, "bf16"), oracle_bits(st.kc, "bf16"))
     assert np.array_equal(bits(g.cache.v_cache, "bf16"), oracle_bits(st.vc, "bf16"))
     say("      whole pool bit-exact after the bulk store")
+    if B == 16:
+        used = sorted({blk for row in g.tables for blk in row})
+        free = sorted(set(range(batch.num_blocks)) - set(used))
+        n = min(len(used), len(free))
+        pairs = np.stack([np.array(used[:n]), np.array(free[:n])], 1).astype(np.int32)
+        pa.copy_blocks(g.cache, torch.from_numpy(pairs).cuda())
+        torch.cuda.synchronize()
+        kc, vc = st.kc.copy(), st.vc.copy()
+        paged.copy_blocks(kc, vc, pairs)
+        assert np.array_equal(bits(g.cache.k_cache, "bf16"), kc)
+        assert np.array_equal(bits(g.cache.v_cache, "bf16"), vc)
+        say(f"      bulk copy of {n} pairs bit-exact over the whole pool")
+        del kc, vc
     del g
     lens = batch.total_lens
-    pick = {int(np.argmax(lens)), int(np.argmin(lens))}
-    pick |= set(int(x) for x in np.random.default_rng(7).choice(len(lens), 6, replace=False))
-    for i in sorted(pick):
-        tab = OS.table_array([st.tables[i]], st.pad_block)
-        ref = paged.decode_attention(st.kc, st.vc, "bf16", batch.q_decode[i:i + 1], "bf16", tab, lens[i:i + 1],
-                                     batch.scale)
-        err = np.max(np.abs(got[i:i + 1] - ref))
-        say(f"      seq {i} (L {int(lens[i])}) max abs err {err:.3e}")
+    tables = OS.table_array(st.tables, st.pad_block)
+    worst = 0.0
+    for i0 in range(0, len(lens), 32):
+        ref = paged.decode_attention(st.kc, st.vc, "bf16", batch.q_decode[i0:i0 + 32], "bf16",
+                                     tables[i0:i0 + 32], lens[i0:i0 + 32], batch.scale)
+        err = np.max(np.abs(got[i0:i0 + 32] - ref))
+        worst = max(worst, err)
+        say(f"      seqs {i0}..{min(i0 + 32, len(lens)) - 1} (L {int(lens[i0:i0 + 32].min())}.."
+            f"{int(lens[i0:i0 + 32].max())}) max abs err {err:.3e}")
         assert err < TOL["bf16"]
+    say(f"      all {len(lens)} sequences: max abs err {worst:.3e}")
 
 
 def test_verify_full_batch():
@@ -767,6 +819,67 @@ def test_verify_full_batch():
     err = np.max(np.abs(got - OS.chunk_ref(batch, OS.build(batch))))
     say(f"      max abs err {err:.3e}")
     assert err < TOL["bf16"]
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_speculative_branches_copy_on_write(kv):
+    """Speculative decoding over copy-on-write branches: a draft branch is
+    forked from each target, its first append copies the shared tail
+    (pa_copy_blocks), the drafts are stored and verified in one
+    pa_prefill_chunk call over the branches, the targets keep the accepted
+    drafts and the branches are released.  Copy pairs, tables, reference
+    counts and the whole pool (bit for bit) match the oracle's run, and so
+    do the verification and the targets' next decode, within tolerance."""
+    from paged_kv_attention_26_amd import runner
+    w = W.spec_branch(kv)
+    say(f"[gpu] speculative branches {w.name}")
+    got = runner.run_spec_branch(w)
+    torch.cuda.synchronize()
+    ref = OS.build_spec_branch(w)
+    assert got.copy_pairs.tolist() == [list(p) for p in ref.copy_pairs]
+    assert len(ref.copy_pairs) == int(np.sum(w.prefix_lens % w.block_size != 0))
+    assert got.branch_tables == ref.branch_tables and got.target_tables == ref.target_tables
+    assert [got.bm.ref_count(b) for b in range(w.num_blocks)] == ref.ref_count
+    assert got.bm.used_blocks == ref.used_blocks
+    assert np.array_equal(bits(got.cache.k_cache, kv), oracle_bits(ref.kc, kv))
+    assert np.array_equal(bits(got.cache.v_cache, kv), oracle_bits(ref.vc, kv))
+    ev = np.max(np.abs(out_f64(got.verify_out) - ref.verify_out))
+    ed = np.max(np.abs(out_f64(got.decode_out) - ref.decode_out))
+    say(f"      {len(ref.copy_pairs)} copies; verify err {ev:.3e}, next decode err {ed:.3e}")
+    assert ev < TOL[kv] and ed < TOL[kv]
+
+
+@pytest.mark.parametrize("kv,B,d", [("bf16", 16, 64), ("bf16", 32, 128), ("f32", 16, 128), ("f32", 32, 128),
+                                    ("f32", 32, 64), ("fp8", 16, 128), ("fp8", 32, 64)])
+def test_copy_blocks_many_pairs_bit_exact(kv, B, d):
+    """pa_copy_blocks with thousands of pairs over pools of 8 kv heads (blocks
+    of 16 KB to 128 KB per pool, so the per-block loop of the larger ones runs
+    several passes), random contents, destinations distinct and never a
+    source, sources repeated: the whole pools bit for bit against the
+    oracle's copy."""
+    from oracle import paged
+    from paged_kv_attention_26_amd import binding as pa
+    Hkv = 8
+    es = {"f32": 4, "bf16": 2, "fp8": 1}[kv]
+    block = Hkv * B * d * es
+    n = min(4000, (192 << 20) // block)
+    nb = 2 * n + 64
+    say(f"[gpu] copy blocks {kv} B{B} d{d}: {n} pairs of {block} B")
+    rng = np.random.default_rng(900 + B + d + es)
+    perm = rng.permutation(nb)
+    pairs = np.stack([rng.choice(perm[n:], n), perm[:n]], 1).astype(np.int32)
+    kb = rng.integers(0, 256, size=(nb, Hkv, B, d * es), dtype=np.uint8)
+    vb = rng.integers(0, 256, size=(nb, Hkv, d, B * es), dtype=np.uint8)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[kv]
+    k = torch.from_numpy(kb).cuda().view(tdt)
+    v = torch.from_numpy(vb).cuda().view(tdt)
+    scale = torch.ones(Hkv, dtype=torch.float32, device="cuda") if kv == "fp8" else None
+    cache = pa.KVCache(k, v, kv, scale, scale)
+    pa.copy_blocks(cache, torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    paged.copy_blocks(kb, vb, pairs)
+    assert np.array_equal(k.view(torch.uint8).cpu().numpy(), kb)
+    assert np.array_equal(v.view(torch.uint8).cpu().numpy(), vb)
 
 
 @pytest.mark.parametrize("kv,small", [("bf16", True), ("fp8", True), ("bf16", False)])

@@ -181,6 +181,34 @@ def config2(small=False) -> PagedBatch:
                        is_chunk=np.zeros(len(lens), bool), rng=rng)
 
 
+def config3_lengths() -> np.ndarray:
+    """The 128 context lengths of the long-context config (its first draw)."""
+    rng = np.random.default_rng(3)
+    return np.round(np.exp(rng.uniform(np.log(128), np.log(32768), size=128))).astype(np.int64)
+
+
+def config3_sample(n=24, seed=303) -> PagedBatch:
+    """A bounded sample of the long-context config for timing the oracle on
+    the host: its first n context lengths, fresh K/V/Q values of the same
+    distribution (seed 303), bf16, B 16, pool 1.25x."""
+    lens = config3_lengths()[:n]
+    rng = np.random.default_rng(seed)
+    return paged_batch("long-context-decode-sample", seed, kv_dtype="bf16", io_dtype="bf16", Hq=32, Hkv=8,
+                       d=128, B=16, prior_lens=lens - 1, new_lens=np.ones(n, np.int64),
+                       is_chunk=np.zeros(n, bool), rng=rng)
+
+
+def store_sample(tokens=16384, seqs=8, seed=304) -> PagedBatch:
+    """A bulk-store sample of the long-context shape for timing the oracle's
+    store on the host: ``seqs`` sequences of tokens / seqs new tokens each
+    (no cached prefix), bf16, Qwen3-8B heads, B 16, pool 1.25x."""
+    rng = np.random.default_rng(seed)
+    n = tokens // seqs
+    return paged_batch("bulk-store-sample", seed, kv_dtype="bf16", io_dtype="bf16", Hq=32, Hkv=8, d=128, B=16,
+                       prior_lens=np.zeros(seqs, np.int64), new_lens=np.full(seqs, n, np.int64),
+                       is_chunk=np.zeros(seqs, bool), rng=rng)
+
+
 def config3(block_size=16, small=False) -> PagedBatch:
     """Long-context decode: 128 seqs, L log-uniform [128, 32768], bf16, split-K 512.
 
@@ -399,3 +427,69 @@ def prefix_agent(small=False, kv_dtype="bf16") -> PrefixAgent:
     return PrefixAgent(name, seed, kv_dtype, "bf16", Hq, Hkv, d, B, nb, free_order, cap, sys_len, user_len,
                        reply_len, turns, join, k_sys, v_sys, k_conv, v_conv, q_all, ks, vs,
                        float(np.float32(1.0 / math.sqrt(d))))
+
+
+@dataclass
+class SpecBranch:
+    """Speculative decoding over copy-on-write branches: every target
+    sequence holds ``prefix_lens[i]`` tokens; a draft branch forked from it
+    appends ``draft`` tokens (its first append copies the shared tail block),
+    a verification chunk attends over the branch, the target then appends
+    the ``accepted[i]`` first draft tokens and the branch is released.
+
+    Rows: ``k_prefix`` / ``v_prefix`` [sum(prefix_lens), Hkv, d] in sequence
+    order; ``k_draft`` / ``v_draft`` [S, draft, Hkv, d]; ``q_verify``
+    [S * draft, Hq, d] (the verification rows, sequence-major); ``q_next``
+    [S, Hq, d] (the target's next decode query)."""
+    name: str
+    seed: int
+    kv_dtype: str
+    io_dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    free_order: np.ndarray
+    prefix_lens: np.ndarray
+    draft: int
+    accepted: np.ndarray
+    k_prefix: np.ndarray
+    v_prefix: np.ndarray
+    k_draft: np.ndarray
+    v_draft: np.ndarray
+    q_verify: np.ndarray
+    q_next: np.ndarray
+    k_scale: Optional[np.ndarray] = None
+    v_scale: Optional[np.ndarray] = None
+    scale: float = 0.0
+
+
+def spec_branch(kv_dtype="bf16", draft=4) -> SpecBranch:
+    """Eight targets with Qwen3-8B layer heads, bf16 or fp8 KV, block 16;
+    prefixes mix partly filled tails (so every branch copies its tail on
+    write), a full tail (the branch opens a new block: no copy) and long
+    contexts; accepted counts 0..draft, fixed so that every case occurs."""
+    seed = 8
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, d, B = 32, 8, 128, 16
+    prefix = np.array([37, 200, 511, 1000, 2049, 64, 3001, 1], dtype=np.int64)
+    accepted = np.array([0, 1, 2, 3, 4, 2, 4, 1], dtype=np.int64)
+    S = len(prefix)
+    # targets and branches at once, plus a block per target for its accepted tokens
+    need = int(sum(math.ceil((int(p) + draft) / B) + 2 for p in prefix))
+    nb = int(math.ceil(1.25 * need))
+    free_order = rng.permutation(nb).astype(np.int64)
+    k_prefix = _values(rng, (int(prefix.sum()), Hkv, d), "bf16")
+    v_prefix = _values(rng, (int(prefix.sum()), Hkv, d), "bf16")
+    k_draft = _values(rng, (S, draft, Hkv, d), "bf16")
+    v_draft = _values(rng, (S, draft, Hkv, d), "bf16")
+    q_verify = _values(rng, (S * draft, Hq, d), "bf16")
+    q_next = _values(rng, (S, Hq, d), "bf16")
+    ks = vs = None
+    if kv_dtype == "fp8":
+        ks, vs = _head_scales(np.concatenate([k_prefix, k_draft.reshape(-1, Hkv, d)]),
+                              np.concatenate([v_prefix, v_draft.reshape(-1, Hkv, d)]))
+    return SpecBranch(f"spec-branch-{kv_dtype}", seed, kv_dtype, "bf16", Hq, Hkv, d, B, nb, free_order, prefix,
+                      draft, accepted, k_prefix, v_prefix, k_draft, v_draft, q_verify, q_next, ks, vs,
+                      float(np.float32(1.0 / math.sqrt(d))))
