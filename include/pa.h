@@ -180,6 +180,24 @@ int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* ou
               int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
               int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* pa_decode without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops or harnesses
+ * that forbid allocation).  Arguments, results and errors as for pa_decode.
+ * The split-K partials and arrival counters live in a device array inside
+ * the library (34 095 104 bytes, the workspace pa_decode needs at its
+ * largest: head_dim 128, groups of 8, 4096 wavefronts); each GPU the library
+ * runs on holds its own copy until the process ends.  The first call on a
+ * device looks its copy up and clears the counters (a small kernel on the
+ * given stream); no call allocates or frees memory.  Every call on one GPU
+ * shares that GPU's array, which keeps the last call's contents (each
+ * completed call leaves the counters at zero): two calls that may run at
+ * the same time on one GPU -- on different streams, or from different
+ * threads -- RACE and give undefined results. */
+int pa_decode_noalloc(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
+                      int32_t num_seqs, int32_t num_q_heads, float scale, const int32_t* block_table,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                      int32_t partition_tokens, void* hip_stream);
+
 /* Timing hook for measurement (no counterpart in the pages): the next
  * pa_decode call made on this thread records start_event and stop_event
  * (hipEvent_t, created by the caller with timing enabled, either may be

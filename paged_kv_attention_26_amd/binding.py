@@ -181,6 +181,29 @@ def decode(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor, context_l
     return out
 
 
+def decode_noalloc(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor, context_lens: torch.Tensor,
+                   max_context_len: int, scale: float, out: Optional[torch.Tensor] = None,
+                   partition_tokens: int = 64, stream=None) -> torch.Tensor:
+    """pa_decode_noalloc: decode with the library's own per-device scratch
+    instead of a workspace (no allocation beyond ``out`` when it is given).
+    Calls that may overlap on one GPU race."""
+    S, Hq, D = q.shape
+    if D != cache.head_dim:
+        raise ValueError("q head_dim does not match the cache")
+    if out is None:
+        out = torch.empty_like(q)
+    if block_table.dim() != 2 or block_table.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_table must be [S, max_blocks] and context_lens [S]")
+    io = DTYPE_CODES["f32"] if cache.dtype == "f32" else DTYPE_CODES["bf16"]
+    L.check(L.lib().pa_decode_noalloc(C.byref(cache.desc), _dev(q, "q", cache.io_dtype), io,
+                                      _dev(out, "out", cache.io_dtype), io, S, Hq, float(scale),
+                                      _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+                                      _dev(context_lens, "context_lens", torch.int32), int(max_context_len),
+                                      int(partition_tokens), _stream(stream)),
+            "pa_decode_noalloc")
+    return out
+
+
 def time_next_decode(start: Optional[torch.cuda.Event], stop: Optional[torch.cuda.Event]) -> None:
     """Arm pa_decode_time_next: the next decode() on this thread records the
     two events with its kernel's own start and end timestamps.  The events

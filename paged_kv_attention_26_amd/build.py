@@ -25,6 +25,7 @@ SOURCES = [
     "decode_fp8.hip",
     "verify.hip",
     "prefill.hip",
+    "noalloc.hip",
 ]
 
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
