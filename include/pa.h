@@ -21,10 +21,18 @@
  *    the last failure on the calling thread is returned by pa_last_error().
  *    Arguments are validated on the host before any HIP call, so a rejected
  *    call launches nothing.
- *  - Values inside device arrays (slots, block ids, lengths) are NOT checked:
- *    a slot >= num_blocks * block_size, a block id >= num_blocks or a
- *    context length above max_blocks_per_seq * block_size reads or writes out
- *    of bounds (undefined behaviour), exactly like an out-of-range index.
+ *  - Values inside device arrays (slots, block ids, lengths, fp8 scales) are
+ *    NOT checked: a slot >= num_blocks * block_size, a block id >=
+ *    num_blocks or a context length above max_blocks_per_seq * block_size
+ *    reads or writes out of bounds (undefined behaviour), exactly like an
+ *    out-of-range index.  With PA_DEBUG_BOUNDS=1 in the environment, every
+ *    call first copies its index arrays (and fp8 scales) to the host on its
+ *    stream, waits, and rejects the call with PA_ERR_BOUNDS, launching
+ *    nothing, if a value is out of range: slots past the pool, block ids of
+ *    a sequence's used blocks outside [0, num_blocks), lengths outside
+ *    [0, max], chunk bounds that do not fit, copy pairs whose dst repeats or
+ *    is also a src, fp8 scales that are not finite and > 0.  (The copies
+ *    synchronise the stream: not for code under graph capture.)
  *  - No C++ exception crosses this interface.
  */
 #ifndef PA_H_
@@ -51,7 +59,8 @@ enum {
   PA_ERR_WORKSPACE = -5,   /* workspace smaller than pa_decode_workspace_bytes() */
   PA_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed         */
   PA_ERR_NO_BLOCKS = -7,   /* block manager: the pool has no free block          */
-  PA_ERR_PENDING = -8      /* block manager: copy pairs are queued (take them)   */
+  PA_ERR_PENDING = -8,     /* block manager: copy pairs are queued (take them)   */
+  PA_ERR_BOUNDS = -9       /* PA_DEBUG_BOUNDS: a device index is out of range    */
 };
 
 /* A paged KV cache (the pools are device memory owned by the caller).
@@ -60,15 +69,19 @@ enum {
  *   k_cache[num_blocks][num_kv_heads][block_size][head_dim]
  *       -- one token's key row of one kv head is contiguous;
  *   v_cache[num_blocks][num_kv_heads][head_dim][block_size]
- *       -- V is stored transposed inside each block: one head-dim column of
- *          a block's tokens is contiguous.
+ *       -- V IS STORED TRANSPOSED inside each block (NOT [block_size]
+ *          [head_dim] like the K pool): one head-dim column of a block's
+ *          tokens is contiguous.  A V pool laid out like the K pool gives
+ *          silently wrong attention; write V only through pa_store_kv /
+ *          pa_copy_blocks, or in this layout.
  * Token t of a sequence lives in physical block table[t / block_size] at
  * offset t % block_size.
  *
  * dtype: PA_F32, PA_BF16 or PA_FP8_E4M3.  For PA_FP8_E4M3 a stored code c of
  * kv head h means c * k_scale[h] (keys) or c * v_scale[h] (values);
- * k_scale / v_scale are device arrays of num_kv_heads fp32 and must be NULL
- * for the other dtypes.
+ * k_scale / v_scale are device arrays of num_kv_heads fp32, each FINITE AND
+ * > 0 (the attention kernels fold them into positive softmax constants), and
+ * must be NULL for the other dtypes.
  * Supported: head_dim in {64, 128}; block_size in {16, 32}. */
 typedef struct {
   void* k_cache;
@@ -227,7 +240,10 @@ int pa_decode_time_next(void* start_event, void* stop_event);
  * probabilities are rounded to bf16 for PV.  Supported: BF16 or FP8_E4M3
  * cache (q and out BF16 either way; an fp8 code of kv head h stands for
  * code * k_scale[h] or code * v_scale[h], converted to bf16 exactly, the
- * scales applied outside the contraction), head_dim 128.
+ * scales applied outside the contraction), head_dim 128.  ONLY THAT SUBSET:
+ * an F32 cache (or F32 q / out) is rejected with PA_ERR_DTYPE and head_dim
+ * 64 with PA_ERR_UNSUPPORTED (decode, store, copy and pack take all three
+ * cache dtypes at both head dims).
  * Chunks of at most 32 / (num_q_heads / num_kv_heads) tokens -- the shape of
  * speculative-decoding verification, k draft tokens plus one -- run on a
  * kernel whose matrix-core columns are the (query head, token) pairs of a
@@ -237,6 +253,28 @@ int pa_prefill_chunk(const pa_kv_cache* cache, const void* q, int32_t q_dtype, v
                      const int32_t* cu_q_lens, const int32_t* seq_lens, const int32_t* block_table,
                      int32_t max_blocks_per_seq, int32_t max_q_len, int32_t max_seq_len,
                      void* hip_stream);
+
+/* Checks of index arrays held in HOST memory (no HIP), the same checks that
+ * PA_DEBUG_BOUNDS=1 runs on every call's device arrays.  Each returns PA_OK
+ * or PA_ERR_BOUNDS (pa_last_error() names the first bad entry); NULL
+ * arrays give PA_ERR_NULL.
+ *   pa_check_slots      : slot_mapping[n] -- every slot < num_blocks * block_size
+ *                         (negative slots are skips)
+ *   pa_check_copy_pairs : src_dst[n][2] -- ids in [0, num_blocks), dst ids
+ *                         distinct, no dst also a src
+ *   pa_check_tables     : lens[num_seqs] in [0, max_len], and the first
+ *                         ceil(len / block_size) entries of each
+ *                         table[num_seqs][max_blocks] row in [0, num_blocks)
+ *   pa_check_chunks     : cu_q_lens[num_seqs + 1] starts at 0, every chunk
+ *                         has 0 .. max_q_len rows and seq_lens[j] >= its rows
+ *   pa_check_scales     : k_scale / v_scale [num_kv_heads] finite and > 0 */
+int pa_check_slots(const pa_kv_cache* cache, const int32_t* slot_mapping, int32_t n);
+int pa_check_copy_pairs(const pa_kv_cache* cache, const int32_t* src_dst, int32_t n);
+int pa_check_tables(const pa_kv_cache* cache, const int32_t* table, int32_t max_blocks, const int32_t* lens,
+                    int32_t num_seqs, int32_t max_len);
+int pa_check_chunks(const pa_kv_cache* cache, const int32_t* cu_q_lens, const int32_t* seq_lens, int32_t num_seqs,
+                    int32_t max_q_len);
+int pa_check_scales(const pa_kv_cache* cache, const float* k_scale, const float* v_scale);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* pa_last_error(void);

@@ -12,12 +12,12 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, \
-    PA_ERR_NO_BLOCKS, PA_ERR_PENDING = 0, -1, -2, -3, -4, -5, -6, -7, -8
+    PA_ERR_NO_BLOCKS, PA_ERR_PENDING, PA_ERR_BOUNDS = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
 ERROR_NAMES = {
     PA_ERR_NULL: "PA_ERR_NULL", PA_ERR_SHAPE: "PA_ERR_SHAPE", PA_ERR_DTYPE: "PA_ERR_DTYPE",
     PA_ERR_UNSUPPORTED: "PA_ERR_UNSUPPORTED", PA_ERR_WORKSPACE: "PA_ERR_WORKSPACE", PA_ERR_HIP: "PA_ERR_HIP",
-    PA_ERR_NO_BLOCKS: "PA_ERR_NO_BLOCKS", PA_ERR_PENDING: "PA_ERR_PENDING",
+    PA_ERR_NO_BLOCKS: "PA_ERR_NO_BLOCKS", PA_ERR_PENDING: "PA_ERR_PENDING", PA_ERR_BOUNDS: "PA_ERR_BOUNDS",
 }
 
 
@@ -50,6 +50,11 @@ SIGNATURES = [
     ("pa_prefill_chunk", C.c_int, [_CACHE, _P, _I, _P, _I, _I, _I, C.c_float, _P, _P, _P, _I, _I, _I, _P]),
     ("pa_pack_kv", C.c_int, [_CACHE, _P, _I, _P, _P, _I, _I, _P, _P, _P]),
     ("pa_last_error", C.c_char_p, []),
+    ("pa_check_slots", C.c_int, [_CACHE, _IP, _I]),
+    ("pa_check_copy_pairs", C.c_int, [_CACHE, _IP, _I]),
+    ("pa_check_tables", C.c_int, [_CACHE, _IP, _I, _IP, _I, _I]),
+    ("pa_check_chunks", C.c_int, [_CACHE, _IP, _IP, _I, _I]),
+    ("pa_check_scales", C.c_int, [_CACHE, C.POINTER(C.c_float), C.POINTER(C.c_float)]),
     ("pa_bm_create", C.c_void_p, [_I, _I, _IP]),
     ("pa_bm_destroy", None, [C.c_void_p]),
     ("pa_bm_seq_new", C.c_int32, [C.c_void_p]),

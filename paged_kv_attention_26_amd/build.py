@@ -19,6 +19,7 @@ BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build", "libpa")
 SOURCES = [
     "api.cpp",
     "block_manager.cpp",
+    "debug_bounds.cpp",
     "store_copy.hip",
     "decode_f32.hip",
     "decode_bf16.hip",

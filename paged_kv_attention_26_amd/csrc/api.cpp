@@ -134,6 +134,10 @@ int pa_store_kv(const pa_kv_cache* cache, const void* k_new, const void* v_new, 
                  : cache->dtype == PA_BF16 ? pa::KV_BF16
                  : raw_fp8                 ? pa::KV_FP8_RAW
                                            : pa::KV_FP8;
+  if (pa::debug_bounds_on()) {
+    rc = pa::debug_check_store(cache, slot_mapping, num_tokens, static_cast<hipStream_t>(hip_stream));
+    if (rc) return rc;
+  }
   hipError_t e = pa::launch_store_kv(a, kv, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "pa_store_kv launch");
   g_err[0] = 0;
@@ -148,6 +152,10 @@ int pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src_dst, int32_t num
   if (!src_dst) return fail(PA_ERR_NULL, "src_dst is NULL");
   pa::CopyArgs a{cache->k_cache, cache->v_cache, src_dst,
                  size_t(cache->num_kv_heads) * cache->block_size * cache->head_dim * elem_bytes(cache->dtype)};
+  if (pa::debug_bounds_on()) {
+    rc = pa::debug_check_copy(cache, src_dst, num_pairs, static_cast<hipStream_t>(hip_stream));
+    if (rc) return rc;
+  }
   hipError_t e = pa::launch_copy_blocks(a, num_pairs, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "pa_copy_blocks launch");
   g_err[0] = 0;
@@ -171,6 +179,11 @@ int pa_pack_kv(const pa_kv_cache* cache, const int32_t* block_table, int32_t max
     return fail(PA_ERR_NULL, "block_table / seq_lens / cu_rows / k_out / v_out is NULL");
   pa::PackArgs a{cache->k_cache, cache->v_cache, block_table, seq_lens, cu_rows, k_out, v_out,
                  cache->num_kv_heads, cache->block_size, cache->head_dim, max_blocks_per_seq};
+  if (pa::debug_bounds_on()) {
+    rc = pa::debug_check_pack(cache, block_table, max_blocks_per_seq, seq_lens, cu_rows, num_seqs, max_seq_len,
+                              static_cast<hipStream_t>(hip_stream));
+    if (rc) return rc;
+  }
   hipError_t e = pa::launch_pack_kv(a, int(elem_bytes(cache->dtype)), num_seqs, int(blocks),
                                     static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "pa_pack_kv launch");
@@ -238,6 +251,11 @@ int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* ou
   const int kv = cache->dtype == PA_F32 ? pa::KV_F32 : cache->dtype == PA_BF16 ? pa::KV_BF16 : pa::KV_FP8;
   const int64_t max_parts = max_context_len > 0 ? (int64_t(max_context_len) + P - 1) / P : 1;
   const int64_t upper_units = int64_t(num_seqs) * cache->num_kv_heads * max_parts;
+  if (pa::debug_bounds_on()) {
+    rc = pa::debug_check_decode(cache, block_table, max_blocks_per_seq, context_lens, num_seqs, max_context_len,
+                                static_cast<hipStream_t>(hip_stream));
+    if (rc) return rc;
+  }
   hipError_t e = pa::launch_decode(a, kv, cache->head_dim, cache->block_size, G, upper_units,
                                    static_cast<hipStream_t>(hip_stream), ev);
   if (e == hipErrorInvalidValue) return fail(PA_ERR_UNSUPPORTED, "no decode kernel for this shape");
@@ -295,6 +313,11 @@ int pa_prefill_chunk(const pa_kv_cache* cache, const void* q, int32_t q_dtype, v
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_q_len = max_q_len;
   const int kv = cache->dtype == PA_BF16 ? pa::KV_BF16 : pa::KV_FP8;
+  if (pa::debug_bounds_on()) {
+    rc = pa::debug_check_prefill(cache, cu_q_lens, seq_lens, block_table, max_blocks_per_seq, num_seqs, max_q_len,
+                                 max_seq_len, static_cast<hipStream_t>(hip_stream));
+    if (rc) return rc;
+  }
   hipError_t e = pa::launch_prefill_chunk(a, kv, cache->block_size, G, static_cast<hipStream_t>(hip_stream));
   if (e == hipErrorInvalidValue) return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for this shape");
   if (e != hipSuccess) return hip_fail(e, "pa_prefill_chunk launch");

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/pa.h"
+
 namespace pa {
 
 // Cache element kinds the kernels are compiled for.
@@ -85,6 +87,20 @@ struct DecodeWorkspace {
 int set_error(int code, const char* fmt, ...);
 
 DecodeWorkspace decode_workspace_layout(int64_t head_dim);
+
+// PA_DEBUG_BOUNDS=1 in the environment: host checks of the values in device
+// index arrays (debug_bounds.cpp).  Each returns PA_OK, or PA_ERR_BOUNDS /
+// PA_ERR_HIP with the message set; they synchronise the stream.
+bool debug_bounds_on();
+int debug_check_scales(const pa_kv_cache* c, hipStream_t s);
+int debug_check_store(const pa_kv_cache* c, const int32_t* slots, int32_t n, hipStream_t s);
+int debug_check_copy(const pa_kv_cache* c, const int32_t* pairs, int32_t n, hipStream_t s);
+int debug_check_decode(const pa_kv_cache* c, const int32_t* table, int32_t max_blocks, const int32_t* lens,
+                       int32_t S, int32_t max_ctx, hipStream_t s);
+int debug_check_prefill(const pa_kv_cache* c, const int32_t* cu, const int32_t* seq_lens, const int32_t* table,
+                        int32_t max_blocks, int32_t S, int32_t max_q, int32_t max_seq, hipStream_t s);
+int debug_check_pack(const pa_kv_cache* c, const int32_t* table, int32_t max_blocks, const int32_t* seq_lens,
+                     const int32_t* cu_rows, int32_t S, int32_t max_seq, hipStream_t s);
 
 hipError_t launch_store_kv(const StoreArgs& a, int kv_kind, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyArgs& a, int num_pairs, hipStream_t s);

@@ -25,7 +25,9 @@
 //  * Scores are formed transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 //    (keys are MFMA rows, queries columns): every lane then owns one query
 //    column, and the softmax statistics and the rescaling of O^T stay in the
-//    lane (one exchange with lane ^ 32 per key tile).
+//    lane (one exchange with lane ^ 32 per key tile, v_permlane32_swap).
+//    The row sum l adds the bf16 probabilities PV multiplies, two per
+//    v_dot2 against ones.
 //  * K rows are loaded into MFMA row m = swap_bits_2_3(key), which makes the
 //    accumulator layout of S^T equal to the B-operand layout of P^T for
 //    O^T = V^T P^T: probabilities go straight from accumulators to bf16
@@ -38,7 +40,10 @@
 //    column's running max grows by more than 2^8 (probabilities stay <= 256).
 //  * The causal mask is applied only on key tiles that reach the diagonal;
 //    keys past the sequence are masked by select and their V rows zeroed,
-//    so NaN in unused slots never reaches the result.
+//    so NaN in unused slots never reaches the result.  The V operands are
+//    read and masked before the next tile's S^T MFMAs are issued, so that
+//    those MFMAs and this tile's exponentials share one basic block and
+//    the forced interleave takes effect.
 //  * Workgroups of one (sequence, kv head) are placed on the same XCD
 //    (workgroup id mod 8), so all query tiles of a sequence share that
 //    XCD's L2 copy of its K/V.
@@ -47,6 +52,17 @@
 #include "pa_internal.h"
 
 namespace pa {
+
+// x of this lane and of lane ^ 32, combined (gfx950 v_permlane32_swap: no
+// LDS round trip).
+__device__ __forceinline__ float max_lane_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_lane_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // LDS swizzle of a key row's 16-byte chunks: chunk c of key row r sits at
 // c ^ kswz(r).  Lane n reads key row swap23(n), so the lanes of any group of
@@ -215,34 +231,37 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
   // position 4 r + (g ^ vphi(r)) holds keys 8g .. 8g + 7 of head dim r, so
   // that the operand reads (lane n: dim 32 dt + n, one g per half wave) fall
   // on distinct 16-byte bank groups in every 8 and every 16 lanes.
-  auto vphi = [](int r) { return ((r >> 1) ^ (r >> 3)) & 3; };
-  auto v_pos = [&](int r, int g) { return 4 * r + (g ^ vphi(r)); };
+  // V^T: keys 0..15 of every head dim in positions 0..255, keys 16..31 in
+  // 256..511, so that each staging load (positions 256 j + tid) reads from
+  // one block at block size 16: position 256 (g / 2) + 2 r + ((g & 1) ^
+  // vphi(r)) holds keys 8g .. 8g + 7 of head dim r.  The operand reads (lane
+  // n: dim 32 dt + n, one g per half wave) then fall on distinct 16-byte bank
+  // groups in every 8 and every 16 lanes.
+  auto vphi = [](int r) { return (r >> 3) & 1; };
+  auto v_pos = [&](int r, int g) { return 256 * (g >> 1) + 2 * r + ((g & 1) ^ vphi(r)); };
   // thread tid fills positions tid and tid + 256 of each tile (lane l of wave
-  // w writes position 256 j + 64 w + l)
-  uint64_t dk_off[2], dv_off[2];
-  bool dk_hi[2], dv_hi[2];
+  // w writes position 256 j + 64 w + l); load j reads block j of the tile at
+  // block size 16 (block 0 at 32), at a per-thread 32-bit offset
+  uint32_t dk_off[2], dv_off[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int pk = tid + 256 * j;
     const int row = pk >> 4, colc = (pk & 15) ^ kswz(row);
-    dk_hi[j] = B != KT && row >= B;
-    dk_off[j] = uint64_t(((row % B) * D + colc * 8) * 2);
-    const int dim = pk >> 2, g = (pk & 3) ^ vphi(pk >> 2);
-    dv_hi[j] = B != KT && 8 * g >= B;
-    dv_off[j] = uint64_t((dim * B + (8 * g) % B) * 2);
+    dk_off[j] = uint32_t(((row % B) * D + colc * 8) * 2);
+    const int dim = tid >> 1, g = 2 * j + ((tid & 1) ^ vphi(tid >> 1));
+    dv_off[j] = uint32_t((dim * B + (8 * g) % B) * 2);
   }
   auto direct_stage = [&](char* base, int id0, int id1) __attribute__((always_inline)) {
     const uint64_t t0_ = (uint64_t(uint32_t(id0)) * uint32_t(Hkv) + uint32_t(kvh)) * kBlockTile;
-    const uint64_t t1_ = (uint64_t(uint32_t(id1)) * uint32_t(Hkv) + uint32_t(kvh)) * kBlockTile;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      char* kb = base + (256 * j + 64 * w) * 16;
-      char* vb = base + KBUF + (256 * j + 64 * w) * 16;
-      __builtin_amdgcn_global_load_lds(kpool + (dk_hi[j] ? t1_ : t0_) + dk_off[j],
-                                       (__attribute__((address_space(3))) void*)kb, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vpool + (dv_hi[j] ? t1_ : t0_) + dv_off[j],
-                                       (__attribute__((address_space(3))) void*)vb, 16, 0, 0);
-    }
+    const uint64_t t1_ = B == KT ? t0_ : (uint64_t(uint32_t(id1)) * uint32_t(Hkv) + uint32_t(kvh)) * kBlockTile;
+    const char* kb0 = kpool + t0_;
+    const char* kb1 = kpool + t1_;
+    const char* vb0 = vpool + t0_;
+    const char* vb1 = vpool + t1_;
+    __builtin_amdgcn_global_load_lds(kb0 + dk_off[0], (__attribute__((address_space(3))) void*)(base + 64 * w * 16), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vb0 + dv_off[0], (__attribute__((address_space(3))) void*)(base + KBUF + 64 * w * 16), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(kb1 + dk_off[1], (__attribute__((address_space(3))) void*)(base + (256 + 64 * w) * 16), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vb1 + dv_off[1], (__attribute__((address_space(3))) void*)(base + KBUF + (256 + 64 * w) * 16), 16, 0, 0);
   };
 
   // ---- Q^T as 8 B operands (k = 16 head dims each): row q0 + t, dims 16s + 8hh .. + 7
@@ -295,7 +314,7 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
       float mt = sc[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = max_lane_xor32(mt);
       const float m_new = fmaxf(m_run, mt);
       // O^T and l are rescaled only when some column's maximum grew by more
       // than 2^8 in exp2 units: until then the stale maximum keeps every
@@ -313,43 +332,18 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
         m_run = m_new;
       }
   };
-  auto probs_pv = [&](int kt, const f32x16_t& sc, const char* sb, f32x16_t& s_next, const char* nsb,
-                      bool do_next) __attribute__((always_inline)) {
+  // V^T operands of tile kt (d-tile dt: dims 32dt + n; key slice ks: keys
+  // k0 + 16ks + 8hh .. + 7), with the rows of keys past the wave's keys
+  // zeroed (NaN poison past the sequence).
+  auto v_operands = [&](int kt, const char* sb, uint4 (&va)[4][2]) __attribute__((always_inline)) {
       const int k0 = kt * KT;
-      if (do_next) s_next = qk_tile(nsb);
-      const float mc = m_run * c;
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -mc));
-        l_run += p[r];
-      }
-      // P^T operands: key slice ks takes accumulators 8ks .. 8ks + 7 (keys k0 + 16ks + 8hh + 0..7)
-      uint4 pb[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        pb[ks] = make_uint4(pack_bf16x2(p[8 * ks + 0], p[8 * ks + 1]), pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]),
-                            pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]), pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7]));
-      if (do_next) {
-        // the next tile's eight K operand reads first, then each of its
-        // eight S^T MFMAs followed by six vector instructions of this tile,
-        // so that the matrix cores work under this wave's own softmax
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
-        }
-      }
-      // V^T operands: d-tile dt (dims 32dt + n), key slice ks (keys k0 + 16ks + 8hh .. + 7)
-      uint4 va[4][2];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
           va[dt][ks] = DIRECT ? *reinterpret_cast<const uint4*>(sb + KBUF + v_pos(32 * dt + n, 2 * ks + hh) * 16)
                               : *reinterpret_cast<const uint4*>(sb + KBUF + (32 * dt + n) * VROW + (16 * ks + 8 * hh) * 2);
-      if (k0 + KT > key_end) {                           // zero V rows of keys past the end (NaN poison)
+      if (k0 + KT > key_end) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int kb = k0 + 16 * ks + 8 * hh;
@@ -361,6 +355,46 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
           for (int dt = 0; dt < 4; ++dt) {
             va[dt][ks].x &= msk[0]; va[dt][ks].y &= msk[1]; va[dt][ks].z &= msk[2]; va[dt][ks].w &= msk[3];
           }
+        }
+      }
+  };
+  // Probabilities of tile kt and O^T += V^T P^T, with the next tile's S^T
+  // (from buffer nsb) issued among the exponentials.  The V operands are
+  // read and masked first, so that the masking branch does not split the
+  // MFMAs from the exponentials.
+  auto probs_pv = [&](int kt, const f32x16_t& sc, const char* sb, f32x16_t& s_next, const char* nsb,
+                      bool do_next) __attribute__((always_inline)) {
+      uint4 va[4][2];
+      v_operands(kt, sb, va);
+      if (do_next) s_next = qk_tile(nsb);
+      float p[16];
+      const float mc = m_run * c;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -mc));
+      // P^T operands: key slice ks takes accumulators 8ks .. 8ks + 7 (keys k0 + 16ks + 8hh + 0..7)
+      uint4 pb[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        pb[ks] = make_uint4(pack_bf16x2(p[8 * ks + 0], p[8 * ks + 1]), pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]),
+                            pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]), pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7]));
+      // l sums the probabilities PV uses: the bf16 pairs, two per v_dot2
+      constexpr uint32_t kOnes = 0x3F803F80u;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        l_run = dot2_bf16(pb[ks].x, kOnes, l_run);
+        l_run = dot2_bf16(pb[ks].y, kOnes, l_run);
+        l_run = dot2_bf16(pb[ks].z, kOnes, l_run);
+        l_run = dot2_bf16(pb[ks].w, kOnes, l_run);
+      }
+      if (do_next) {
+        // the next tile's eight K operand reads first, then each of its
+        // eight S^T MFMAs followed by six vector instructions of this tile,
+        // so that the matrix cores work under this wave's own softmax
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
         }
       }
 #pragma unroll
@@ -469,7 +503,7 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
 #undef PA_STAGE_STORE
 
   // ---- normalise and store: accumulator r of d-tile dt is dim 32dt + 8(r/4) + 4hh + (r%4)
-  const float l = l_run + __shfl_xor(l_run, 32);
+  const float l = sum_lane_xor32(l_run);
   if (!valid_q) return;
   const float inv = v_mul / l;
   uint16_t* orow = static_cast<uint16_t*>(a.out) + (size_t(q0 + t) * Hq + head) * D + 4 * hh;

@@ -352,3 +352,89 @@ def test_native_prefix_cache_rejects_bad_arguments():
     assert n.prefix_insert(s, [0] * 16) == 0      # already cached
     n.set_prefix_capacity(0)                      # off again: evicts every entry
     assert n.ref_count(n.block_table(s)[0]) == 1
+
+
+# ------------------------------------------- host checks of index arrays (pa_check_*)
+def _ip(a):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return a, a.ctypes.data_as(C.POINTER(C.c_int32))
+
+
+def test_check_slots_flags_the_first_slot_past_the_pool():
+    lib, c = L.lib(), cache(num_blocks=8, block_size=16)
+    a, p = _ip([0, 5, -1, 127, -7])
+    assert lib.pa_check_slots(C.byref(c), p, len(a)) == L.PA_OK        # negative slots are skips
+    a, p = _ip([0, 5, 128, 3])
+    assert lib.pa_check_slots(C.byref(c), p, len(a)) == L.PA_ERR_BOUNDS
+    assert b"slot_mapping[2] = 128" in lib.pa_last_error()
+    assert lib.pa_check_slots(None, p, 4) == L.PA_ERR_NULL
+
+
+@pytest.mark.parametrize("pairs,ok", [
+    ([[0, 1], [0, 2], [3, 4]], True),            # one source copied twice
+    ([[0, 1], [2, 1]], False),                   # a repeated destination
+    ([[0, 1], [1, 2]], False),                   # a chain: 1 is a dst and a src
+    ([[0, 8]], False), ([[-1, 2]], False),       # outside the pool
+])
+def test_check_copy_pairs(pairs, ok):
+    lib, c = L.lib(), cache(num_blocks=8)
+    a, p = _ip(pairs)
+    assert lib.pa_check_copy_pairs(C.byref(c), p, len(pairs)) == (L.PA_OK if ok else L.PA_ERR_BOUNDS)
+
+
+def test_check_tables_reads_only_the_used_entries():
+    lib, c = L.lib(), cache(num_blocks=8, block_size=16)
+    table, tp = _ip([[3, 7, 99, -5], [1, 2, 4, 6]])       # row 0 uses 2 blocks: 99 and -5 are padding
+    lens, lp = _ip([17, 64])
+    assert lib.pa_check_tables(C.byref(c), tp, 4, lp, 2, 64) == L.PA_OK
+    lens, lp = _ip([33, 64])                                # row 0 now needs its third entry (99)
+    assert lib.pa_check_tables(C.byref(c), tp, 4, lp, 2, 64) == L.PA_ERR_BOUNDS
+    assert b"block_table[0][2] = 99" in lib.pa_last_error()
+    lens, lp = _ip([17, 65])                                # longer than max_len
+    assert lib.pa_check_tables(C.byref(c), tp, 4, lp, 2, 64) == L.PA_ERR_BOUNDS
+    assert lib.pa_check_tables(C.byref(c), tp, 4, lp, 2, 80) == L.PA_ERR_BOUNDS   # 5 blocks > row of 4
+    lens, lp = _ip([-1, 0])
+    assert lib.pa_check_tables(C.byref(c), tp, 4, lp, 2, 64) == L.PA_ERR_BOUNDS
+
+
+def test_check_chunks():
+    lib, c = L.lib(), cache()
+    cu, cp = _ip([0, 5, 5, 12])
+    sl, sp = _ip([9, 0, 7])
+    assert lib.pa_check_chunks(C.byref(c), cp, sp, 3, 7) == L.PA_OK
+    assert lib.pa_check_chunks(C.byref(c), cp, sp, 3, 6) == L.PA_ERR_BOUNDS     # a chunk of 7 rows
+    sl, sp = _ip([9, 0, 6])                                                      # shorter than its chunk
+    assert lib.pa_check_chunks(C.byref(c), cp, sp, 3, 7) == L.PA_ERR_BOUNDS
+    cu, cp = _ip([1, 5, 5, 12])
+    assert lib.pa_check_chunks(C.byref(c), cp, sp, 3, 7) == L.PA_ERR_BOUNDS
+    cu, cp = _ip([0, 5, 4, 12])                                                  # decreasing
+    sl, sp = _ip([9, 9, 9])
+    assert lib.pa_check_chunks(C.byref(c), cp, sp, 3, 8) == L.PA_ERR_BOUNDS
+
+
+@pytest.mark.parametrize("bad", [0.0, -1.0, float("inf"), float("nan")])
+def test_check_scales(bad):
+    lib, c = L.lib(), cache(num_kv_heads=2)
+    good = (C.c_float * 2)(0.5, 0.25)
+    assert lib.pa_check_scales(C.byref(c), good, good) == L.PA_OK
+    assert lib.pa_check_scales(C.byref(c), (C.c_float * 2)(0.5, bad), good) == L.PA_ERR_BOUNDS
+    assert lib.pa_check_scales(C.byref(c), good, (C.c_float * 2)(bad, 0.5)) == L.PA_ERR_BOUNDS
+
+
+@pytest.mark.parametrize("dtype,d,q_io,code", [
+    (L.PA_F32, 128, L.PA_F32, L.PA_ERR_DTYPE),             # fp32 cache: no prefill kernel
+    (L.PA_F32, 64, L.PA_F32, L.PA_ERR_DTYPE),
+    (L.PA_BF16, 64, L.PA_BF16, L.PA_ERR_UNSUPPORTED),      # head_dim 64: no prefill kernel
+    (L.PA_FP8_E4M3, 64, L.PA_BF16, L.PA_ERR_UNSUPPORTED),
+    (L.PA_BF16, 128, L.PA_F32, L.PA_ERR_DTYPE),            # q / out must be bf16
+])
+def test_prefill_subset_is_rejected_with_its_code(dtype, d, q_io, code):
+    """pa_prefill_chunk runs over bf16 or fp8 caches at head_dim 128; every
+    other combination is rejected on the host with a fixed code."""
+    lib = L.lib()
+    kw = dict(head_dim=d, num_kv_heads=8, dtype=dtype)
+    if dtype == L.PA_FP8_E4M3:
+        kw.update(k_scale=FAKE, v_scale=FAKE)
+    c = cache(**kw)
+    args = [FAKE, q_io, FAKE, q_io, 2, 32, 0.088, FAKE, FAKE, FAKE, 64, 512, 1024, None]
+    assert lib.pa_prefill_chunk(C.byref(c), *args) == code

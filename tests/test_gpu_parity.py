@@ -821,6 +821,56 @@ def test_verify_full_batch():
     assert err < TOL["bf16"]
 
 
+def test_debug_bounds_mode(monkeypatch):
+    """PA_DEBUG_BOUNDS=1: every call first checks the values in its device
+    index arrays on the host.  Valid calls give the same bits as without the
+    checks; calls with a planted bad value are rejected with PA_ERR_BOUNDS
+    before any launch.  (The planted values are ones that would stay inside
+    the pools even if launched: a repeated copy destination, a context length
+    above max_context_len over a table that covers it, a negative fp8 scale.
+    Slots past the pool are covered on the CPU, by pa_check_slots.)"""
+    from paged_kv_attention_26_amd import _lib as L, binding as pa, runner
+    say("[gpu] PA_DEBUG_BOUNDS")
+    batch = W.config2(small=True)
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    want = runner.decode_step(g).clone()
+    wk, wv = runner.pack_all(g)
+    cb = W.config4(small=True, kv_dtype="fp8")
+    gc = runner.prepare(cb)
+    runner.store_step(gc)
+    wc = runner.chunk_step(gc).clone()
+    torch.cuda.synchronize()
+    monkeypatch.setenv("PA_DEBUG_BOUNDS", "1")
+    runner.store_step(g)                                        # the same rows again: same bits
+    got = runner.decode_step(g)
+    k, v = runner.pack_all(g)
+    gotc = runner.chunk_step(gc)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    assert torch.equal(k.view(torch.int16), wk.view(torch.int16)) and torch.equal(v.view(torch.int16), wv.view(torch.int16))
+    assert torch.equal(gotc.view(torch.int16), wc.view(torch.int16))
+    d = g.dec
+    with pytest.raises(L.PaError) as e:                         # a length above max_context_len
+        pa.decode(g.cache, d["q"], d["table"], d["lens"], d["max_len"] - 1, batch.scale)
+    assert e.value.code == L.PA_ERR_BOUNDS
+    used = sorted({b for row in g.tables for b in row})
+    free = [b for b in range(batch.num_blocks) if b not in set(used)]
+    before = bits(g.cache.k_cache, "bf16").copy()
+    with pytest.raises(L.PaError) as e:                         # one destination twice
+        pa.copy_blocks(g.cache, torch.tensor([[used[0], free[0]], [used[1], free[0]]], dtype=torch.int32,
+                                             device="cuda"))
+    assert e.value.code == L.PA_ERR_BOUNDS
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(g.cache.k_cache, "bf16"), before)   # nothing was launched
+    gc.cache.k_scale[0] = -1.0                                  # an fp8 scale below zero
+    c = gc.dec
+    with pytest.raises(L.PaError) as e:
+        pa.decode(gc.cache, c["q"], c["table"], c["lens"], c["max_len"], cb.scale)
+    assert e.value.code == L.PA_ERR_BOUNDS
+    say("      valid calls bit-identical; planted values rejected before launch")
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_speculative_branches_copy_on_write(kv):
     """Speculative decoding over copy-on-write branches: a draft branch is
