@@ -75,6 +75,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only-extra", choices=EXTRA_GROUPS, default=None,
                     help="run only this group of secondary measurements and print them (for profiling)")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="only measure the HBM reference kernels (streaming read, copy, random 4 KB tiles)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB device buffer 4 times (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -113,7 +115,40 @@ def timed_calls(fn, reps=50, warm=5, flush=True):
     return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
 
 
-EXTRA_GROUPS = ("long_context", "mixed", "fork", "verify", "handoff")
+EXTRA_GROUPS = ("long_context", "mixed", "fork", "verify", "handoff", "hbm_probe")
+
+
+def hbm_probe(torch):
+    """Practical HBM ceilings on this GPU from the reference kernels of
+    libpa_probe.so: a streaming read of 4 GiB, a copy of 2 GiB (read + write
+    counted), and whole 4 KB tiles of a 4 GiB buffer read once each in a
+    seeded random order (decode's access pattern).  Median of 20 calls, each
+    after a cache flush."""
+    import ctypes as C
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_attention_26_amd", "libpa_probe.so")
+    lib = C.CDLL(path)
+    lib.pa_probe_read.argtypes = [C.c_void_p, C.c_size_t, C.c_int, C.c_void_p, C.c_void_p]
+    lib.pa_probe_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_void_p]
+    lib.pa_probe_tiles.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int, C.c_void_p, C.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = cus * 8
+    stream = lambda: C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    big = torch.zeros(1 << 32, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(grid * 256, dtype=torch.int32, device="cuda")
+    out = {}
+    med, _, _ = timed_calls(lambda: lib.pa_probe_read(big.data_ptr(), big.numel(), grid, sink.data_ptr(), stream()), 20)
+    out["stream_read_4GiB"] = dict(GBps=round(big.numel() / med / 1e6, 1), ms=round(med, 4))
+    half = big.numel() // 2
+    med, _, _ = timed_calls(lambda: lib.pa_probe_copy(big.data_ptr(), big.data_ptr() + half, half, grid, stream()), 20)
+    out["copy_2GiB_read_plus_write"] = dict(GBps=round(2 * half / med / 1e6, 1), ms=round(med, 4))
+    n_tiles = big.numel() // 4096
+    order = torch.from_numpy(np.random.default_rng(11).permutation(n_tiles).astype(np.int32)).cuda()
+    med, _, _ = timed_calls(lambda: lib.pa_probe_tiles(big.data_ptr(), order.data_ptr(), n_tiles, cus * 4,
+                                                       sink.data_ptr(), stream()), 20)
+    out["random_4KB_tiles_read_4GiB"] = dict(GBps=round(big.numel() / med / 1e6, 1), ms=round(med, 4))
+    del big, sink, order
+    torch.cuda.empty_cache()
+    return out
 
 
 def extras(pa, runner, W, torch, groups=EXTRA_GROUPS):
@@ -190,6 +225,8 @@ def extras(pa, runner, W, torch, groups=EXTRA_GROUPS):
                                            frac=round((2 * byt + 4 * rows) / med_u / 1e6 / HBM_PEAK_GBS, 4),
                                            ms=round(med_u, 4))
         del g, gd
+    if "hbm_probe" in groups:
+        out["hbm_probe"] = hbm_probe(torch)
     if "fork" in groups:
         fb = W.config5()
         gf = runner.run_fork(fb)
@@ -440,6 +477,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_per_launch": n, "launches": 4}), flush=True)
+        return
+    if args.hbm_probe:
+        print(json.dumps({"hbm_probe": hbm_probe(torch)}), flush=True)
         return
     import workloads as W
     from paged_kv_attention_26_amd import binding as pa, runner

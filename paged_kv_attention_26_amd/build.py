@@ -29,6 +29,11 @@ SOURCES = [
     "noalloc.hip",
 ]
 
+# HBM reference kernels, a library of their own (measurement only, no part of
+# libpa's C ABI): the benchmark's --hbm-probe mode and its hbm_probe group
+PROBE_SOURCES = ["hbm_probe.hip"]
+PROBE_OUT = os.path.join(HERE, "libpa_probe.so")
+
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 COMMON = [
@@ -65,19 +70,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out, verbose):
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(f"[build] wrote {OUT}")
+        print(f"[build] wrote {out}")
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], OUT, verbose)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_OUT, verbose)
     return OUT
 
 

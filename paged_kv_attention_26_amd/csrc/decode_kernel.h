@@ -10,7 +10,9 @@
 // How (a bandwidth kernel; the pages' CUDA design is not available and is
 // not followed):
 //  * Work is cut into units = (sequence, kv head, partition of part_tokens
-//    tokens), ordered sequence-major.  Every wavefront takes an equal,
+//    tokens), ordered sequence-major.  Every wave finds its range from the
+//    prefix of the units over the sequences: built in each wave's own
+//    registers for at most 64 sequences, in LDS by the workgroup beyond.  Every wavefront takes an equal,
 //    contiguous range of units (a static split of the whole batch, so ragged
 //    lengths cannot unbalance the waves), and runs its online softmax across
 //    consecutive partitions of one (sequence, kv head).  One wave serves the
@@ -59,6 +61,7 @@
 #ifndef PA_DECODE_STEP_TOKENS
 #define PA_DECODE_STEP_TOKENS 64
 #endif
+
 
 namespace pa {
 
@@ -138,6 +141,17 @@ __device__ __forceinline__ void build_prefix(const int32_t* lens, int S, int PT,
   }
   if (tid == 255) s_prefix[S] = s_tmp[255];
   __syncthreads();
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
 }
 
 // Largest s with s_prefix[s] <= key (s_prefix strictly increasing, s_prefix[0] == 0).
@@ -263,12 +277,34 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
   const int S = a.num_seqs;
   const int PT = a.part_tokens;
   int* s_len = s_prefix + S + 1;
-  build_prefix(context_lens, S, PT, s_prefix, s_len, s_tmp);
-
   const int lane = threadIdx.x & 63;
+  // The unit prefix over the sequences: for at most 64 sequences every wave
+  // builds it in its own registers (lane i: sequence i's length and the
+  // units before it), with no LDS and no barrier; larger batches build it in
+  // LDS with the whole workgroup.
+  const bool wave_prefix = S <= 64;
+  int r_len = 0, r_ex = 0, total_units;
+  if (wave_prefix) {
+    r_len = lane < S ? max(0, context_lens[lane]) : 0;
+    const int u = lane < S ? units_of(r_len, PT) : 0;
+    const int incl = wave_incl_scan(u);
+    r_ex = incl - u;
+    total_units = uniform(__builtin_amdgcn_readlane(incl, 63));
+  } else {
+    build_prefix(context_lens, S, PT, s_prefix, s_len, s_tmp);
+    total_units = s_prefix[S];
+  }
+  // length and first unit of sequence sq (wave-uniform)
+  auto len_of = [&](int sq) -> int {
+    return wave_prefix ? __builtin_amdgcn_readlane(r_len, sq) : uniform(s_len[sq]);
+  };
+  auto prefix_of = [&](int sq) -> int {
+    return wave_prefix ? __builtin_amdgcn_readlane(r_ex, sq) : s_prefix[sq];
+  };
+
   const int w = uniform(threadIdx.x >> 6);                // wave-uniform, so all range math stays scalar
   const int Hkv = a.num_kv_heads, Hq = a.num_q_heads;
-  const int64_t U = int64_t(s_prefix[S]) * Hkv;
+  const int64_t U = int64_t(total_units) * Hkv;
   // at most U waves: every range is non-empty, so every wave from the first
   // to the last of a split item holds a partial of it
   const int64_t W = min<int64_t>(a.total_waves, U);
@@ -299,7 +335,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
     bool live, any;             // any: some step of the range was ever found
   };
   auto seg_setup = [&](Cursor& c) {                          // derive the segment's steps
-    const int L = uniform(s_len[c.seq]);
+    const int L = len_of(c.seq);
     const int nu = units_of(L, PT);
     c.p_end = int(min<int64_t>(nu, c.part + (u_end - c.u)));
     const int t_begin = c.part * PT, t_end = min(L, c.p_end * PT);
@@ -382,11 +418,17 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
   };
 
   // first unit of the range -> (sequence, kv head, partition)
-  int seq = find_seq(s_prefix, S, int(u / Hkv));
+  int seq;
+  if (wave_prefix) {                                      // the last sequence whose prefix is <= the key
+    const int key = int(u / Hkv);
+    seq = uniform(__builtin_popcountll(__ballot(lane < S && r_ex <= key))) - 1;
+  } else {
+    seq = find_seq(s_prefix, S, int(u / Hkv));
+  }
   int kvh, part;
   {
-    const int nu = units_of(uniform(s_len[seq]), PT);
-    const int r = int(u - int64_t(s_prefix[seq]) * Hkv);
+    const int nu = units_of(len_of(seq), PT);
+    const int r = int(u - int64_t(prefix_of(seq)) * Hkv);
     kvh = uniform(r / nu);
     part = uniform(r - kvh * nu);
   }
@@ -457,7 +499,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
   bool first = true;
   bool q_ready = false;                                      // qfn / qpn hold this segment's query
   for (;;) {                                                 // one (sequence, kv head) segment per pass
-    const int L = uniform(s_len[seq]);
+    const int L = len_of(seq);
     const int nu = units_of(L, PT);
     const int p_end = int(min<int64_t>(nu, part + (u_end - u)));
     const bool whole = part == 0 && p_end == nu;
@@ -693,7 +735,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
           for (int j = 0; j < C::VLB; ++j) xstore(a.part_acc + (base + g) * D + j * C::DPL + vd, acc[g][j]);
         }
       }
-      const int64_t u0 = int64_t(s_prefix[seq]) * Hkv + int64_t(kvh) * nu;
+      const int64_t u0 = int64_t(prefix_of(seq)) * Hkv + int64_t(kvh) * nu;
       const int w0 = owner_wave(u0, U, W);
       const int w1 = owner_wave(u0 + nu - 1, U, W);
       pend[slot] = Pending{seq, kvh, w0, w1 - w0 + 1, w1, int64_t(w0) * U / W == u0};

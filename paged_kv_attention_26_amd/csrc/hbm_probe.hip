@@ -1,0 +1,74 @@
+// HBM reference kernels for measurement only (libpa_probe.so, loaded by the
+// benchmark's --hbm-probe mode; not part of libpa's C ABI).  They give the
+// practical ceilings the attention and store kernels are compared with:
+//  * probe_read: a streaming read of a buffer, 16 bytes per lane per load;
+//  * probe_copy: a streaming copy (read + write);
+//  * probe_tiles: reads of whole 4 KB tiles in a seeded random order (the
+//    access pattern of decode: one (block, kv head) tile per wave load).
+// Each kernel folds what it reads into one value per thread, stored only if
+// it equals a key the data never holds, so no load can be dropped and
+// nothing but the copy writes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+__global__ void __launch_bounds__(256) probe_read(const uint4* __restrict__ src, size_t n16, uint32_t key,
+                                                  uint32_t* __restrict__ sink) {
+  uint32_t acc = 0;
+  const size_t stride = size_t(gridDim.x) * 256;
+  size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == key) sink[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+__global__ void __launch_bounds__(256) probe_copy(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n16) {
+  const size_t stride = size_t(gridDim.x) * 256;
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+// Wave w reads tiles order[w], order[w + waves], ... (4 KB each: 64 lanes x
+// 4 x 16 bytes).
+__global__ void __launch_bounds__(256) probe_tiles(const uint4* __restrict__ src, const int32_t* __restrict__ order,
+                                                   int32_t n_tiles, uint32_t key, uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int waves = gridDim.x * 4;
+  uint32_t acc = 0;
+  for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < n_tiles; t += waves) {
+    const uint4* p = src + size_t(order[t]) * 256;
+    const uint4 a = p[lane], b = p[lane + 64], c = p[lane + 128], d = p[lane + 192];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  if (acc == key) sink[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+}  // namespace
+
+// Host launchers (plain C, device pointers).  grid: workgroups of 256
+// threads; sink: at least grid * 256 uint32 of device memory.
+extern "C" int pa_probe_read(const void* src, size_t bytes, int grid, void* sink, void* stream) {
+  hipLaunchKernelGGL(probe_read, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(src), bytes / 16, 0xA5A5A5A5u, static_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+extern "C" int pa_probe_copy(const void* src, void* dst, size_t bytes, int grid, void* stream) {
+  hipLaunchKernelGGL(probe_copy, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(src), static_cast<uint4*>(dst), bytes / 16);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// order: n_tiles int32 tile indices, each < bytes of src / 4096.
+extern "C" int pa_probe_tiles(const void* src, const int32_t* order, int32_t n_tiles, int grid, void* sink,
+                              void* stream) {
+  hipLaunchKernelGGL(probe_tiles, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(src), order, n_tiles, 0xA5A5A5A5u, static_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
