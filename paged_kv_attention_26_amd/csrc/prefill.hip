@@ -43,7 +43,9 @@
 //    so NaN in unused slots never reaches the result.  The V operands are
 //    read and masked before the next tile's S^T MFMAs are issued, so that
 //    those MFMAs and this tile's exponentials share one basic block and
-//    the forced interleave takes effect.
+//    the forced interleave takes effect.  For a bf16 cache the next tile's K
+//    operands are read from LDS at the start of the step, so that their
+//    latency passes under this tile's masking and maximum.
 //  * Workgroups of one (sequence, kv head) are placed on the same XCD
 //    (workgroup id mod 8), so all query tiles of a sequence share that
 //    XCD's L2 copy of its K/V.
@@ -291,15 +293,21 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
   // exponentials.  Every wave runs every tile of its workgroup: a tile past
   // a wave's own keys is masked whole (probabilities 0, V rows zeroed),
   // which leaves its results bit for bit as they would be without it.
-  auto qk_tile = [&](const char* sb) __attribute__((always_inline)) -> f32x16_t {
-    uint4 ka[8];
+  auto read_k = [&](const char* sb, uint4 (&ka)[8]) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < 8; ++s)
       ka[s] = *reinterpret_cast<const uint4*>(sb + my_key * KROW + ((2 * s + hh) ^ kswz(my_key)) * 16);
+  };
+  auto qk_mfma = [&](const uint4 (&ka)[8]) __attribute__((always_inline)) -> f32x16_t {
     f32x16_t sc = f32x16_t{};
 #pragma unroll
     for (int st = 0; st < 8; ++st) sc = mfma32(ka[st], qb[st], sc);
     return sc;
+  };
+  auto qk_tile = [&](const char* sb) __attribute__((always_inline)) -> f32x16_t {
+    uint4 ka[8];
+    read_k(sb, ka);
+    return qk_mfma(ka);
   };
   auto mask_rescale = [&](int kt, f32x16_t& sc) __attribute__((always_inline)) {
       const int k0 = kt * KT;
@@ -362,11 +370,13 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
   // (from buffer nsb) issued among the exponentials.  The V operands are
   // read and masked first, so that the masking branch does not split the
   // MFMAs from the exponentials.
+  // ka_next: the next tile's K operands when they were read earlier (else
+  // null: they are read here)
   auto probs_pv = [&](int kt, const f32x16_t& sc, const char* sb, f32x16_t& s_next, const char* nsb,
-                      bool do_next) __attribute__((always_inline)) {
+                      bool do_next, const uint4 (*ka_next)[8]) __attribute__((always_inline)) {
       uint4 va[4][2];
       v_operands(kt, sb, va);
-      if (do_next) s_next = qk_tile(nsb);
+      if (do_next) s_next = ka_next ? qk_mfma(*ka_next) : qk_tile(nsb);
       float p[16];
       const float mc = m_run * c;
 #pragma unroll
@@ -390,7 +400,7 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
         // the next tile's eight K operand reads first, then each of its
         // eight S^T MFMAs followed by six vector instructions of this tile,
         // so that the matrix cores work under this wave's own softmax
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+        if (!ka_next) __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
@@ -439,8 +449,10 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
     tile_ids(min((KT_) + 4, last), j0, j1);                                                            \
     {                                                                                                  \
       f32x16_t s_nxt;                                                                                  \
+      uint4 ka_n[8];                                                                                   \
+      read_k(NXT, ka_n);                 /* next tile's K operands: their latency under the max */     \
       mask_rescale((KT_), s_cur);                                                                      \
-      probs_pv((KT_), s_cur, CUR, s_nxt, NXT, true);                                                   \
+      probs_pv((KT_), s_cur, CUR, s_nxt, NXT, true, &ka_n);                                            \
       s_cur = s_nxt;                                                                                   \
     }
     for (int kt = 0; kt < n_tiles_wg; kt += 4) {
@@ -479,7 +491,7 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
   {                                                                                                   \
     f32x16_t s_nxt;                                                                                   \
     mask_rescale((KT_), s_cur);                                                                       \
-    probs_pv((KT_), s_cur, CUR, s_nxt, NXT, true);                                                    \
+    probs_pv((KT_), s_cur, CUR, s_nxt, NXT, true, nullptr);                                           \
     s_cur = s_nxt;                                                                                    \
   }                                                                                                   \
   PA_STAGE_STORE(ST, SBUF);                                  /* tile KT_ + 2 */                        \
