@@ -1,8 +1,9 @@
 // HBM reference kernels for measurement only (libpa_probe.so, loaded by the
 // benchmark's --hbm-probe mode; not part of libpa's C ABI).  They give the
 // practical ceilings the attention and store kernels are compared with:
-//  * probe_read: a streaming read of a buffer, 16 bytes per lane per load;
-//  * probe_copy: a streaming copy (read + write);
+//  * probe_read: a streaming read of a buffer, 16 bytes per lane per load,
+//    each workgroup reading one contiguous stretch;
+//  * probe_copy: a streaming copy (read + write), in the same stretches;
 //  * probe_tiles: reads of whole 4 KB tiles in a seeded random order (the
 //    access pattern of decode: one (block, kv head) tile per wave load).
 // Each kernel folds what it reads into one value per thread, stored only if
@@ -13,25 +14,40 @@
 
 namespace {
 
+// Workgroup b streams the contiguous stretch [b n16 / grid, (b + 1) n16 / grid)
+// of 16-byte chunks, each thread with eight loads in flight (the stretch is
+// walked in rounds of 8 x 256 chunks; the remainder one chunk at a time).
 __global__ void __launch_bounds__(256) probe_read(const uint4* __restrict__ src, size_t n16, uint32_t key,
                                                   uint32_t* __restrict__ sink) {
+  const size_t lo = size_t(blockIdx.x) * n16 / gridDim.x, hi = size_t(blockIdx.x + 1) * n16 / gridDim.x;
   uint32_t acc = 0;
-  const size_t stride = size_t(gridDim.x) * 256;
-  size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  size_t i = lo + threadIdx.x;
+  for (; i + 7 * 256 < hi; i += 8 * 256) {
+    uint4 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = src[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
   }
-  for (; i < n16; i += stride) {
+  for (; i < hi; i += 256) {
     const uint4 a = src[i];
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   if (acc == key) sink[blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+// Same stretches as probe_read, four 16-byte loads in flight per thread.
 __global__ void __launch_bounds__(256) probe_copy(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n16) {
-  const size_t stride = size_t(gridDim.x) * 256;
-  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+  const size_t lo = size_t(blockIdx.x) * n16 / gridDim.x, hi = size_t(blockIdx.x + 1) * n16 / gridDim.x;
+  size_t i = lo + threadIdx.x;
+  for (; i + 3 * 256 < hi; i += 4 * 256) {
+    uint4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = src[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dst[i + u * 256] = x[u];
+  }
+  for (; i < hi; i += 256) dst[i] = src[i];
 }
 
 // Wave w reads tiles order[w], order[w + waves], ... (4 KB each: 64 lanes x

@@ -43,9 +43,9 @@
 //    so NaN in unused slots never reaches the result.  The V operands are
 //    read and masked before the next tile's S^T MFMAs are issued, so that
 //    those MFMAs and this tile's exponentials share one basic block and
-//    the forced interleave takes effect.  For a bf16 cache the next tile's K
-//    operands are read from LDS at the start of the step, so that their
-//    latency passes under this tile's masking and maximum.
+//    the forced interleave takes effect.  The next tile's K operands are
+//    read from LDS at the start of the step, so that their latency passes
+//    under this tile's masking and maximum.
 //  * Workgroups of one (sequence, kv head) are placed on the same XCD
 //    (workgroup id mod 8), so all query tiles of a sequence share that
 //    XCD's L2 copy of its K/V.
@@ -86,15 +86,14 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
   constexpr int QT = 32;                 // query rows per wave
   constexpr int KT = 32;                 // keys per tile
   constexpr int KROW = D * 2;            // LDS bytes per key row; 16-byte chunks XOR-swizzled by kswz(row)
-  constexpr int VROW = KT * 2 + 16;      // LDS bytes per head-dim row of the transposed value tile
   constexpr int KBUF = KT * KROW;
-  constexpr int BUF = KBUF + D * VROW;
   // A bf16 cache is staged straight from memory into LDS (16-byte loads to
-  // LDS) through a ring of four unpadded buffers; an fp8 cache goes through
-  // registers, converted to bf16, into a ring of three padded buffers.
+  // LDS) through a ring of four buffers; an fp8 cache goes through
+  // registers, converted to bf16, into a ring of three.  Both use the same
+  // unpadded layout.
   constexpr bool DIRECT = KV == KV_BF16;
   constexpr int RBUF = KBUF + D * KT * 2;                  // ring buffer: K tile, then V^T tile
-  __shared__ __attribute__((aligned(16))) char smem[3][DIRECT ? 16 : BUF];   // ring of three (fp8)
+  __shared__ __attribute__((aligned(16))) char smem[3][DIRECT ? 16 : RBUF];  // ring of three (fp8)
   __shared__ __attribute__((aligned(16))) char ring0[DIRECT ? RBUF : 16];
   __shared__ __attribute__((aligned(16))) char ring1[DIRECT ? RBUF : 16];
   __shared__ __attribute__((aligned(16))) char ring2[DIRECT ? RBUF : 16];
@@ -173,10 +172,10 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
   const float c = KV == KV_FP8 ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
   const float v_mul = KV == KV_FP8 ? a.v_scale[kvh] : 1.f;
 
-  // ---- staging of one tile by the whole workgroup: each thread moves NCH
-  // 16-byte chunks of K (chunk i: row i / 16, column chunk i % 16) and NCH of
-  // V^T (chunk i: head dim i / 4, 8-key group i % 4), chunks tid and
-  // tid + 64 * kPrefillWaves.
+  // ---- staging of one tile by the whole workgroup through registers (fp8):
+  // each thread moves NCH chunks of 8 elements of K (chunk i: row i / 16,
+  // column chunk i % 16) and NCH of V^T (the chunk that the ring layout below
+  // puts at LDS position i), chunks tid and tid + 64 * kPrefillWaves.
   constexpr int NCH = KT * 16 / (kPrefillWaves * 64);
   static_assert(NCH * kPrefillWaves * 64 == KT * 16 && NCH * kPrefillWaves * 64 == D * 4 && NCH <= 2,
                 "whole chunks of K and V per thread");
@@ -187,12 +186,18 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
   // last block again (tile_ids clamps), so every address stays inside an
   // allocated block; those keys are masked.
   constexpr uint64_t kBlockTile = uint64_t(B) * D * ES;    // bytes of one (block, kv head) tile
+  // V^T position i holds keys 8 g .. 8 g + 7 of head dim (i % 256) / 2 (see
+  // the ring layout): consecutive lanes write consecutive 16-byte positions,
+  // free of bank conflicts.
+  auto vphi = [](int r) { return (r >> 3) & 1; };
+  auto v_dim = [](int i) { return (i & 255) >> 1; };
+  auto v_grp = [&](int i) { return 2 * (i >> 8) + ((i & 1) ^ vphi(v_dim(i))); };
   auto k_lane = [&](int i) { return uint64_t((((i >> 4) % B) * D + (i & 15) * 8) * ES); };
-  auto v_lane = [&](int i) { return uint64_t(((i >> 2) * B + (8 * (i & 3)) % B) * ES); };
+  auto v_lane = [&](int i) { return uint64_t((v_dim(i) * B + (8 * v_grp(i)) % B) * ES); };
   auto k_hi = [&](int i) { return B != KT && (i >> 4) >= B; };
-  auto v_hi = [&](int i) { return B != KT && 8 * (i & 3) >= B; };
+  auto v_hi = [&](int i) { return B != KT && 8 * v_grp(i) >= B; };
   auto k_lds = [&](int i) { return (i >> 4) * KROW + ((i & 15) ^ kswz(i >> 4)) * 16; };
-  auto v_lds = [&](int i) { return KBUF + (i >> 2) * VROW + (i & 3) * 16; };
+  auto v_lds = [&](int i) { return KBUF + i * 16; };
   const int ci0 = tid, ci1 = tid + kPrefillWaves * 64;
   const uint64_t k_lane0 = k_lane(ci0), k_lane1 = k_lane(ci1), v_lane0 = v_lane(ci0), v_lane1 = v_lane(ci1);
   const bool k_hi0 = k_hi(ci0), k_hi1 = k_hi(ci1), v_hi0 = v_hi(ci0), v_hi1 = v_hi(ci1);
@@ -226,20 +231,16 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
     id1 = table[min(b0 + 1, kmax / B)];
   };
 
-  // Ring layout.  A load to LDS puts lane l's 16 bytes at the wave's base +
-  // 16 l, so the layout is chosen per LDS position and each lane loads the
-  // chunk that belongs there.  K: position 16 r + (c ^ kswz(r)) holds chunk c
-  // of key row r (the padded layout's swizzle, rows of 256 bytes).  V^T:
-  // position 4 r + (g ^ vphi(r)) holds keys 8g .. 8g + 7 of head dim r, so
-  // that the operand reads (lane n: dim 32 dt + n, one g per half wave) fall
-  // on distinct 16-byte bank groups in every 8 and every 16 lanes.
-  // V^T: keys 0..15 of every head dim in positions 0..255, keys 16..31 in
-  // 256..511, so that each staging load (positions 256 j + tid) reads from
-  // one block at block size 16: position 256 (g / 2) + 2 r + ((g & 1) ^
-  // vphi(r)) holds keys 8g .. 8g + 7 of head dim r.  The operand reads (lane
-  // n: dim 32 dt + n, one g per half wave) then fall on distinct 16-byte bank
-  // groups in every 8 and every 16 lanes.
-  auto vphi = [](int r) { return (r >> 3) & 1; };
+  // Ring layout (16-byte positions).  A load to LDS puts lane l's 16 bytes
+  // at the wave's base + 16 l, so the layout is chosen per LDS position and
+  // each lane loads the chunk that belongs there.  K: position 16 r + (c ^
+  // kswz(r)) holds chunk c of key row r (rows of 256 bytes).  V^T: keys
+  // 0..15 of every head dim in positions 0..255, keys 16..31 in 256..511, so
+  // that each staging load (positions 256 j + tid) reads from one block at
+  // block size 16: position 256 (g / 2) + 2 r + ((g & 1) ^ vphi(r)) holds
+  // keys 8g .. 8g + 7 of head dim r.  The operand reads (lane n: dim 32 dt +
+  // n, one g per half wave) then fall on distinct 16-byte bank groups in
+  // every 8 and every 16 lanes.
   auto v_pos = [&](int r, int g) { return 256 * (g >> 1) + 2 * r + ((g & 1) ^ vphi(r)); };
   // thread tid fills positions tid and tid + 256 of each tile (lane l of wave
   // w writes position 256 j + 64 w + l); load j reads block j of the tile at
@@ -286,10 +287,10 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
   // before its own MFMAs and written to LDS one tile before them, so about
   // two tiles of MFMA work cover each load's latency.  Tiles past the last
   // re-read the last one.
-  // A tile in three parts.  qk_tile: S^T = K Q^T (A: lane row n = key
-  // k0 + my_key, dims 16s + 8hh).  mask_rescale: causal and end masks, the
-  // tile maximum and the lazy rescale.  probs_pv: probabilities and
-  // O^T += V^T P^T, with the next tile's qk_tile issued among its
+  // A tile in three parts.  read_k + qk_mfma: S^T = K Q^T (A: lane row n =
+  // key k0 + my_key, dims 16s + 8hh).  mask_rescale: causal and end masks,
+  // the tile maximum and the lazy rescale.  probs_pv: probabilities and
+  // O^T += V^T P^T, with the next tile's S^T MFMAs issued among its
   // exponentials.  Every wave runs every tile of its workgroup: a tile past
   // a wave's own keys is masked whole (probabilities 0, V rows zeroed),
   // which leaves its results bit for bit as they would be without it.
@@ -349,8 +350,7 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          va[dt][ks] = DIRECT ? *reinterpret_cast<const uint4*>(sb + KBUF + v_pos(32 * dt + n, 2 * ks + hh) * 16)
-                              : *reinterpret_cast<const uint4*>(sb + KBUF + (32 * dt + n) * VROW + (16 * ks + 8 * hh) * 2);
+          va[dt][ks] = *reinterpret_cast<const uint4*>(sb + KBUF + v_pos(32 * dt + n, 2 * ks + hh) * 16);
       if (k0 + KT > key_end) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -367,16 +367,14 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
       }
   };
   // Probabilities of tile kt and O^T += V^T P^T, with the next tile's S^T
-  // (from buffer nsb) issued among the exponentials.  The V operands are
-  // read and masked first, so that the masking branch does not split the
-  // MFMAs from the exponentials.
-  // ka_next: the next tile's K operands when they were read earlier (else
-  // null: they are read here)
-  auto probs_pv = [&](int kt, const f32x16_t& sc, const char* sb, f32x16_t& s_next, const char* nsb,
-                      bool do_next, const uint4 (*ka_next)[8]) __attribute__((always_inline)) {
+  // (from its K operands ka_next, read earlier) issued among the
+  // exponentials.  The V operands are read and masked first, so that the
+  // masking branch does not split the MFMAs from the exponentials.
+  auto probs_pv = [&](int kt, const f32x16_t& sc, const char* sb, f32x16_t& s_next,
+                      const uint4 (&ka_next)[8]) __attribute__((always_inline)) {
       uint4 va[4][2];
       v_operands(kt, sb, va);
-      if (do_next) s_next = ka_next ? qk_mfma(*ka_next) : qk_tile(nsb);
+      s_next = qk_mfma(ka_next);
       float p[16];
       const float mc = m_run * c;
 #pragma unroll
@@ -396,16 +394,13 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
         l_run = dot2_bf16(pb[ks].z, kOnes, l_run);
         l_run = dot2_bf16(pb[ks].w, kOnes, l_run);
       }
-      if (do_next) {
-        // the next tile's eight K operand reads first, then each of its
-        // eight S^T MFMAs followed by six vector instructions of this tile,
-        // so that the matrix cores work under this wave's own softmax
-        if (!ka_next) __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+      // each of the next tile's eight S^T MFMAs followed by six vector
+      // instructions of this tile, so that the matrix cores work under this
+      // wave's own softmax
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
-        }
+      for (int r = 0; r < 8; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
@@ -452,7 +447,7 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
       uint4 ka_n[8];                                                                                   \
       read_k(NXT, ka_n);                 /* next tile's K operands: their latency under the max */     \
       mask_rescale((KT_), s_cur);                                                                      \
-      probs_pv((KT_), s_cur, CUR, s_nxt, NXT, true, &ka_n);                                            \
+      probs_pv((KT_), s_cur, CUR, s_nxt, ka_n);                                                        \
       s_cur = s_nxt;                                                                                   \
     }
     for (int kt = 0; kt < n_tiles_wg; kt += 4) {
@@ -490,8 +485,10 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
   tile_ids(min((KT_) + 4, last), j0, j1);                                                             \
   {                                                                                                   \
     f32x16_t s_nxt;                                                                                   \
+    uint4 ka_n[8];                                                                                    \
+    read_k(NXT, ka_n);                                                                                \
     mask_rescale((KT_), s_cur);                                                                       \
-    probs_pv((KT_), s_cur, CUR, s_nxt, NXT, true, nullptr);                                           \
+    probs_pv((KT_), s_cur, CUR, s_nxt, ka_n);                                                         \
     s_cur = s_nxt;                                                                                    \
   }                                                                                                   \
   PA_STAGE_STORE(ST, SBUF);                                  /* tile KT_ + 2 */                        \

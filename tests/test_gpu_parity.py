@@ -463,14 +463,21 @@ def test_fp8_fork_store_copy_and_decode(small):
     # forked beams read identical blocks before divergence.  Decoded one at a
     # time (the same launch for each), their outputs are bit-identical.  In one
     # batch the work is split differently for each beam, and probabilities
-    # are rounded to bf16 against the running maximum of each piece, so the
-    # beams agree only to that rounding (far inside the oracle tolerance).
+    # are rounded to bf16 (relative error <= 2^-9 each) against the running
+    # maximum of each piece.  Over ~2k weights that reweighting moves the fp32
+    # result by ~1e-4 at most in expectation; the bound allows 2^-12 for it,
+    # plus up to two bf16 ulps of the value for the final rounding on either
+    # side (a result may cross a binade).
     b0 = snap["one"][0].view(torch.int16)
     for b in range(1, fb.beams):
         assert torch.equal(snap["one"][b].view(torch.int16), b0)
     one = snap["one"][0][0].float()
+    ulp = torch.ldexp(torch.ones_like(one), torch.frexp(one)[1] - 8)      # bf16 ulp of |one|
+    drift = max(float((snap["out"][b].float() - one).abs().max()) for b in range(fb.beams))
+    say(f"      batched beams vs one-at-a-time: max abs drift {drift:.3e}")
     for b in range(fb.beams):
-        assert float((snap["out"][b].float() - one).abs().max()) < 1e-2, b
+        excess = (snap["out"][b].float() - one).abs() - (2 * ulp + 2.0 ** -12)
+        assert float(excess.max()) <= 0, b
     ref = OS.fork_decode_ref(fb, st)
     err = np.max(np.abs(out_f64(out) - ref))
     say(f"      max abs err {err:.3e}")
