@@ -32,8 +32,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0       # published dense bf16 matrix peak
 # and WRITE_SIZE passes scaled by the same counters on a plain 1 GiB copy
 # (bench.py --copy-probe 1024), and the hash of the kernel sources they were
 # taken on: once those sources change the figure no longer applies.
-DECODE_TRAFFIC = {"sources_sha256": "f862b40bf4b8b2a618349774811e6b8e2063a9ca36a134ad03b764a35402194d",
-                  "bytes_per_launch": 305715764}
+DECODE_TRAFFIC = {"sources_sha256": "1f6c5b29c91828990b7828d69cf8d2b935636f8d449c9dea4ce9a32e694e2b06",
+                  "bytes_per_launch": 305720416}
 DECODE_SOURCES = ("decode_kernel.h", "pa_device.h", "pa_internal.h", "decode_bf16.hip")
 
 
