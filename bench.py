@@ -32,8 +32,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0       # published dense bf16 matrix peak
 # and WRITE_SIZE passes scaled by the same counters on a plain 1 GiB copy
 # (bench.py --copy-probe 1024), and the hash of the kernel sources they were
 # taken on: once those sources change the figure no longer applies.
-DECODE_TRAFFIC = {"sources_sha256": "1f6c5b29c91828990b7828d69cf8d2b935636f8d449c9dea4ce9a32e694e2b06",
-                  "bytes_per_launch": 305720416}
+DECODE_TRAFFIC = {"sources_sha256": "cde09573bb0a6ddda467d464ddb4e12705df8ad10e3336f492a1fbd0cdf33319",
+                  "bytes_per_launch": 305806926}
 DECODE_SOURCES = ("decode_kernel.h", "pa_device.h", "pa_internal.h", "decode_bf16.hip")
 
 
@@ -79,6 +79,10 @@ def parse():
                     help="only measure the HBM reference kernels (streaming read, copy, random 4 KB tiles)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB device buffer 4 times (calibrates HBM byte counters)")
+    ap.add_argument("--decode-trace", action="store_true",
+                    help="only record per-wave phase times of the headline decode kernel (libpa_trace.so)")
+    ap.add_argument("--decode-trace-out", default=None, metavar="NPY",
+                    help="with --decode-trace: also save the raw records [launch][wave][16] (uint32) there")
     return ap.parse_args()
 
 
@@ -149,6 +153,85 @@ def hbm_probe(torch):
     del big, sink, order
     torch.cuda.empty_cache()
     return out
+
+
+def decode_trace(args, torch):
+    """Per-wave phase times of the headline decode kernel, from the
+    measurement build libpa_trace.so (the same kernel with s_memrealtime
+    stamps, 100 MHz).  Each of args.steps launches (after args.warmup) runs
+    alone: store of the step, then pa_decode with a trace buffer armed, then a
+    synchronisation.  Times are microseconds from the launch's first wave
+    start; medians over the waves of a launch, then over the launches."""
+    import ctypes as C
+    from paged_kv_attention_26_amd import _lib
+    _lib.LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_attention_26_amd",
+                                 "libpa_trace.so")
+    _lib._lib = None
+    lib = _lib.lib()
+    lib.pa_decode_trace_next.restype = C.c_int
+    lib.pa_decode_trace_next.argtypes = [C.c_void_p]
+    import workloads as W
+    from paged_kv_attention_26_amd import binding as pa, runner
+    layers = []
+    for li in range(args.layers):
+        b = W.config2()
+        if li:
+            b.free_order = np.random.default_rng(1000 + li).permutation(b.num_blocks)
+        layers.append(runner.prepare(b))
+    d0 = layers[0].dec
+    ws = pa.decode_workspace(len(d0["idx"]), layers[0].batch.num_q_heads, layers[0].batch.head_dim, d0["max_len"],
+                             args.partition)
+    out = torch.empty_like(d0["q"])
+    buf = torch.zeros(4096 * 16, dtype=torch.int32, device="cuda")
+    recs = []
+    for i in range(args.warmup + args.steps):
+        g = layers[i % len(layers)]
+        runner.store_step(g)
+        buf.zero_()
+        _lib.check(lib.pa_decode_trace_next(C.c_void_p(buf.data_ptr())), "pa_decode_trace_next")
+        runner.decode_step(g, out=out, partition_tokens=args.partition, workspace=ws)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            r = buf.view(-1, 16).cpu().numpy().astype(np.int64)
+            recs.append(r[r[:, 0] != 0])
+    med = lambda x: float(np.median(x))
+    per = []
+    for r in recs:
+        t0 = r[:, 0].min()
+        t = (r[:, :6] - t0) / 100.0                         # us
+        ids_req, ids = (r[:, 14] - t0) / 100.0, (r[:, 15] - t0) / 100.0
+        arrived = np.where(r[:, 13] != 0, (r[:, 13] - t0) / 100.0, np.nan)
+        xcc = r[:, 7] & 15
+        merged = r[:, 10] != 0
+        end = t[:, 5]
+        per.append(dict(
+            waves=len(r), kernel_end=end.max(), start_last=t[:, 0].max(), start_med=med(t[:, 0]),
+            prefix_med=med(t[:, 1]), ids_req_med=med(ids_req), ids_med=med(ids), ids_max=ids.max(),
+            issue_med=med(t[:, 2]), issue_max=t[:, 2].max(), step1_med=med(t[:, 3]),
+            range_end_med=med(t[:, 4]), range_end_max=t[:, 4].max(), end_med=med(end),
+            step_us_med=med((t[:, 4] - t[:, 3]) / np.maximum(r[:, 9] - 1, 1)),
+            merged_frac=float(merged.mean()), end_med_merging=med(end[merged]) if merged.any() else float("nan"),
+            count_in_us_med=float(np.nanmedian(arrived - t[:, 4])),
+            merge_us_med=float(np.nanmedian((end - arrived)[merged])) if merged.any() else float("nan"),
+            end_med_not_merging=med(end[~merged]),
+            two_seg_frac=float((r[:, 8] >= 2).mean()),
+            xcd_range_end_med=[med(t[xcc == x, 4]) if (xcc == x).any() else float("nan") for x in range(8)],
+            xcd_is_block_mod_8=bool(np.all(xcc == (r[:, 6] & 7))),
+            steps=(int(r[:, 9].min()), med(r[:, 9]), int(r[:, 9].max()))))
+    if args.decode_trace_out:
+        n = max(len(r) for r in recs)
+        raw = np.zeros((len(recs), n, 16), np.uint32)
+        for i, r in enumerate(recs):
+            raw[i, :len(r)] = r
+        np.save(args.decode_trace_out, raw)
+    keys = [k for k in per[0] if k not in ("xcd_range_end_med", "steps", "waves", "xcd_is_block_mod_8")]
+    summ = {k: round(med([p[k] for p in per]), 2) for k in keys}
+    summ["xcd_range_end_med"] = [round(med([p["xcd_range_end_med"][x] for p in per]), 1) for x in range(8)]
+    summ["waves"] = per[0]["waves"]
+    summ["steps_min_med_max"] = per[0]["steps"]
+    summ["xcd_is_block_mod_8"] = all(p["xcd_is_block_mod_8"] for p in per)
+    summ["kernel_end_per_launch"] = [round(p["kernel_end"], 1) for p in per]
+    return {"decode_trace": summ, "launches": len(per)}
 
 
 def extras(pa, runner, W, torch, groups=EXTRA_GROUPS):
@@ -480,6 +563,9 @@ def main():
         return
     if args.hbm_probe:
         print(json.dumps({"hbm_probe": hbm_probe(torch)}), flush=True)
+        return
+    if args.decode_trace:
+        print(json.dumps(decode_trace(args, torch)), flush=True)
         return
     import workloads as W
     from paged_kv_attention_26_amd import binding as pa, runner

@@ -34,6 +34,12 @@ SOURCES = [
 PROBE_SOURCES = ["hbm_probe.hip"]
 PROBE_OUT = os.path.join(HERE, "libpa_probe.so")
 
+# A measurement build of libpa whose bf16 decode kernels record per-wave time
+# stamps (PA_DECODE_TRACE; pa_decode_trace_next arms a buffer): the
+# benchmark's --decode-trace mode.  Only these sources differ from libpa.
+TRACE_SOURCES = ["api.cpp", "decode_bf16.hip"]
+TRACE_OUT = os.path.join(HERE, "libpa_trace.so")
+
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 COMMON = [
@@ -55,9 +61,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: libpa needs ROCm's hipcc to build")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, defines=()) -> str:
+    tag = "".join("." + d.lower() for d in defines)
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + tag + ".o")
+    cmd = [hipcc(), *COMMON, *("-D" + d for d in defines), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -83,12 +90,15 @@ def _link(objs, out, verbose):
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = SOURCES + PROBE_SOURCES
-    jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
+    jobs_in = [(s, ()) for s in SOURCES + PROBE_SOURCES] + [(s, ("PA_DECODE_TRACE",)) for s in TRACE_SOURCES]
+    jobs = min(len(jobs_in), int(os.environ.get("MAX_JOBS", "8")))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = dict(zip(srcs, ex.map(_compile, srcs)))
-    _link([objs[s] for s in SOURCES], OUT, verbose)
-    _link([objs[s] for s in PROBE_SOURCES], PROBE_OUT, verbose)
+        done = list(ex.map(lambda j: _compile(*j), jobs_in))
+    objs = {j: o for j, o in zip(jobs_in, done)}
+    _link([objs[(s, ())] for s in SOURCES], OUT, verbose)
+    _link([objs[(s, ())] for s in PROBE_SOURCES], PROBE_OUT, verbose)
+    _link([objs[(s, ("PA_DECODE_TRACE",))] if s in TRACE_SOURCES else objs[(s, ())] for s in SOURCES], TRACE_OUT,
+          verbose)
     return OUT
 
 

@@ -20,6 +20,10 @@ namespace {
 thread_local char g_err[512] = "";
 // events armed by pa_decode_time_next for this thread's next pa_decode call
 thread_local pa::LaunchEvents g_decode_events;
+#ifdef PA_DECODE_TRACE
+// trace buffer armed by pa_decode_trace_next (measurement build only)
+thread_local uint32_t* g_decode_trace = nullptr;
+#endif
 
 template <typename... A>
 int fail(int code, const char* fmt, A... args) {
@@ -248,6 +252,10 @@ int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* ou
   a.num_kv_heads = cache->num_kv_heads;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.part_tokens = P;
+#ifdef PA_DECODE_TRACE
+  a.trace = g_decode_trace;                                // armed for this call only
+  g_decode_trace = nullptr;
+#endif
   const int kv = cache->dtype == PA_F32 ? pa::KV_F32 : cache->dtype == PA_BF16 ? pa::KV_BF16 : pa::KV_FP8;
   const int64_t max_parts = max_context_len > 0 ? (int64_t(max_context_len) + P - 1) / P : 1;
   const int64_t upper_units = int64_t(num_seqs) * cache->num_kv_heads * max_parts;
@@ -269,6 +277,17 @@ int pa_decode_time_next(void* start_event, void* stop_event) {
   g_err[0] = 0;
   return PA_OK;
 }
+
+#ifdef PA_DECODE_TRACE
+// Measurement build only (libpa_trace.so): the next pa_decode call on this
+// thread writes 16 uint32 of time stamps per wave into buf (device memory of
+// at least 4096 * 64 bytes).
+int pa_decode_trace_next(void* buf) {
+  g_decode_trace = static_cast<uint32_t*>(buf);
+  g_err[0] = 0;
+  return PA_OK;
+}
+#endif
 
 int pa_prefill_chunk(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
                      int32_t num_seqs, int32_t num_q_heads, float scale, const int32_t* cu_q_lens,

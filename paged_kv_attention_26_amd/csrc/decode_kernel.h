@@ -62,6 +62,21 @@
 #define PA_DECODE_STEP_TOKENS 64
 #endif
 
+// A measurement build (PA_DECODE_TRACE) records per-wave time stamps of the
+// decode kernel's phases (the 100 MHz constant clock of s_memrealtime) into
+// DecodeArgs::trace; in the library itself the stamps compile to nothing.
+// Record of wave w (16 uint32 at trace + 16 w): stamps of its start, unit
+// prefix, first tiles issued, first step done, range done, end (after its
+// merges and their stores); XCD (workgroup id mod 8), hardware XCC id,
+// segments, steps, merged items (bits), pending items (bits), early
+// count-in; stamps of the count-in done, first block ids requested and
+// arrived.
+#ifdef PA_DECODE_TRACE
+#define PA_TRACE_STAMP(v) ((v) = uint32_t(__builtin_amdgcn_s_memrealtime()))
+#else
+#define PA_TRACE_STAMP(v) ((void)0)
+#endif
+
 
 namespace pa {
 
@@ -278,6 +293,13 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
   const int PT = a.part_tokens;
   int* s_len = s_prefix + S + 1;
   const int lane = threadIdx.x & 63;
+  // trace stamps: start, prefix, first tiles issued, first step done, range
+  // done, end; segments, steps
+  [[maybe_unused]] uint32_t tr_start = 0, tr_prefix = 0, tr_issue = 0, tr_step1 = 0, tr_range = 0, tr_end = 0;
+  [[maybe_unused]] uint32_t tr_ids_req = 0, tr_ids = 0;   // first block ids requested, arrived
+  [[maybe_unused]] uint32_t tr_arrived = 0;               // counted in on the split items
+  [[maybe_unused]] uint32_t tr_nseg = 0, tr_nstep = 0;
+  PA_TRACE_STAMP(tr_start);
   // The unit prefix over the sequences: for at most 64 sequences every wave
   // builds it in its own registers (lane i: sequence i's length and the
   // units before it), with no LDS and no barrier; larger batches build it in
@@ -294,6 +316,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
     build_prefix(context_lens, S, PT, s_prefix, s_len, s_tmp);
     total_units = s_prefix[S];
   }
+  PA_TRACE_STAMP(tr_prefix);
   // length and first unit of sequence sq (wave-uniform)
   auto len_of = [&](int sq) -> int {
     return wave_prefix ? __builtin_amdgcn_readlane(r_len, sq) : uniform(s_len[sq]);
@@ -459,10 +482,15 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
   Cursor nx{u, seq, kvh, part, 0, 0, 0, 0, 0, true, false};
   seg_setup(nx);
   skip_empty(nx);
+  PA_TRACE_STAMP(tr_ids_req);
   int ids_nx[C::BPC];
   cursor_ids(nx, ids_nx);
   int kvh_nx = nx.kvh;
   load_q(qf, qp, seq, kvh);
+#ifdef PA_DECODE_TRACE
+  __builtin_amdgcn_s_waitcnt(0xC07F);                       // lgkmcnt(0): the block ids are in
+  PA_TRACE_STAMP(tr_ids);
+#endif
   // The query and block ids must be in registers before the first tile is
   // requested; an explicit wait here keeps the compiler from waiting on every
   // in-flight tile (vmcnt(0)) at each step.
@@ -472,6 +500,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
   __builtin_amdgcn_sched_barrier(0);
   load_v(ids_nx, kvh_nx);
   __builtin_amdgcn_sched_barrier(0);
+  PA_TRACE_STAMP(tr_issue);
   advance(nx);
   cursor_ids(nx, ids_nx);
   kvh_nx = nx.kvh;
@@ -686,9 +715,19 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
       kvh_nx = nx.kvh;
       nx_bytes = nx.live ? uint32_t(kTile) : 0u;
     };
-    for (int st = 0; st + 1 < nsteps; ++st) do_step(st, std::false_type{});
+    for (int st = 0; st + 1 < nsteps; ++st) {
+      do_step(st, std::false_type{});
+#ifdef PA_DECODE_TRACE
+      if (tr_step1 == 0) PA_TRACE_STAMP(tr_step1);
+#endif
+    }
     q_ready = nsteps > 0;
     if (nsteps > 0) do_step(nsteps - 1, std::true_type{});
+#ifdef PA_DECODE_TRACE
+    if (tr_step1 == 0) PA_TRACE_STAMP(tr_step1);
+    ++tr_nseg;
+    tr_nstep += uint32_t(nsteps);
+#endif
 
     // ---- finish the segment
     float l[G];
@@ -759,14 +798,34 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
     }
   }
 
+  PA_TRACE_STAMP(tr_range);
+  [[maybe_unused]] uint32_t tr_merged = 0;
   // Count in on the split items; the last wave to arrive at one merges it.
   if (has_pend[0] || has_pend[1]) {
     bool last0, last1;
     arrive_last2(a.arrivals + pend[0].w1, pend[0].n, has_pend[0], early, a.arrivals + pend[1].w1, pend[1].n,
                  has_pend[1], last0, last1);
+    PA_TRACE_STAMP(tr_arrived);
     if (last0) merge_split<D, G, C::F32>(a, pend[0].seq, pend[0].kvh, pend[0].w0, pend[0].n, pend[0].w0_first);
     if (last1) merge_split<D, G, C::F32>(a, pend[1].seq, pend[1].kvh, pend[1].w0, pend[1].n, pend[1].w0_first);
+#ifdef PA_DECODE_TRACE
+    tr_merged = (last0 ? 1u : 0u) | (last1 ? 2u : 0u);
+#endif
   }
+#ifdef PA_DECODE_TRACE
+  __builtin_amdgcn_s_waitcnt(0);                            // the wave's last stores have completed
+  PA_TRACE_STAMP(tr_end);
+  if (a.trace && lane == 0) {
+    // XCC_ID (hardware register 20, bits 3:0): the XCD this wave runs on
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20);
+    const uint32_t rec[16] = {tr_start, tr_prefix, tr_issue, tr_step1, tr_range, tr_end,
+                              uint32_t(blockIdx.x & 7), xcc, tr_nseg, tr_nstep, tr_merged,
+                              uint32_t(has_pend[0]) | (uint32_t(has_pend[1]) << 1), uint32_t(early),
+                              tr_arrived, tr_ids_req, tr_ids};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a.trace[size_t(wid) * 16 + i] = rec[i];
+  }
+#endif
 }
 
 // A launch whose events take the kernel's own start and end timestamps.

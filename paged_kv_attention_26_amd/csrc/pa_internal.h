@@ -58,6 +58,9 @@ struct DecodeArgs {
   float scale_log2;   // softmax scale * log2(e)
   int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq;
   int32_t part_tokens, total_waves;  // total_waves is set by the launcher
+  // [total_waves][16] per-wave time stamps, written only by kernels built
+  // with PA_DECODE_TRACE (a measurement build); null otherwise
+  uint32_t* trace;
 };
 
 // Upper bound on the waves one decode launch uses (the workspace is sized for it).
