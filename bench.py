@@ -83,6 +83,9 @@ def parse():
                     help="only record per-wave phase times of the headline decode kernel (libpa_trace.so)")
     ap.add_argument("--decode-trace-out", default=None, metavar="NPY",
                     help="with --decode-trace: also save the raw records [launch][wave][16] (uint32) there")
+    ap.add_argument("--decode-trace-workload", default="layer", choices=("layer", "long16", "long32"),
+                    help="with --decode-trace: the Qwen3-8B layer (default) or the long-context batch at block "
+                         "16 / 32 (512-token partitions, a cache flush before each launch)")
     return ap.parse_args()
 
 
@@ -159,9 +162,10 @@ def decode_trace(args, torch):
     """Per-wave phase times of the headline decode kernel, from the
     measurement build libpa_trace.so (the same kernel with s_memrealtime
     stamps, 100 MHz).  Each of args.steps launches (after args.warmup) runs
-    alone: store of the step, then pa_decode with a trace buffer armed, then a
-    synchronisation.  Times are microseconds from the launch's first wave
-    start; medians over the waves of a launch, then over the launches."""
+    alone: the step's store (the layer) or a cache flush (long context), then
+    pa_decode with a trace buffer armed, then a synchronisation.  Times are
+    microseconds from the launch's first wave start; medians over the waves of
+    a launch, then over the launches."""
     import ctypes as C
     from paged_kv_attention_26_amd import _lib
     _lib.LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_attention_26_amd",
@@ -172,24 +176,34 @@ def decode_trace(args, torch):
     lib.pa_decode_trace_next.argtypes = [C.c_void_p]
     import workloads as W
     from paged_kv_attention_26_amd import binding as pa, runner
+    long_ctx = args.decode_trace_workload != "layer"
+    part = 512 if long_ctx else args.partition
     layers = []
-    for li in range(args.layers):
-        b = W.config2()
-        if li:
-            b.free_order = np.random.default_rng(1000 + li).permutation(b.num_blocks)
-        layers.append(runner.prepare(b))
+    if long_ctx:
+        g = runner.prepare(W.config3(16 if args.decode_trace_workload == "long16" else 32))
+        runner.store_step(g)
+        layers.append(g)
+    else:
+        for li in range(args.layers):
+            b = W.config2()
+            if li:
+                b.free_order = np.random.default_rng(1000 + li).permutation(b.num_blocks)
+            layers.append(runner.prepare(b))
     d0 = layers[0].dec
     ws = pa.decode_workspace(len(d0["idx"]), layers[0].batch.num_q_heads, layers[0].batch.head_dim, d0["max_len"],
-                             args.partition)
+                             part)
     out = torch.empty_like(d0["q"])
     buf = torch.zeros(4096 * 16, dtype=torch.int32, device="cuda")
     recs = []
     for i in range(args.warmup + args.steps):
         g = layers[i % len(layers)]
-        runner.store_step(g)
+        if long_ctx:
+            flush_caches()
+        else:
+            runner.store_step(g)
         buf.zero_()
         _lib.check(lib.pa_decode_trace_next(C.c_void_p(buf.data_ptr())), "pa_decode_trace_next")
-        runner.decode_step(g, out=out, partition_tokens=args.partition, workspace=ws)
+        runner.decode_step(g, out=out, partition_tokens=part, workspace=ws)
         torch.cuda.synchronize()
         if i >= args.warmup:
             r = buf.view(-1, 16).cpu().numpy().astype(np.int64)
@@ -231,7 +245,7 @@ def decode_trace(args, torch):
     summ["steps_min_med_max"] = per[0]["steps"]
     summ["xcd_is_block_mod_8"] = all(p["xcd_is_block_mod_8"] for p in per)
     summ["kernel_end_per_launch"] = [round(p["kernel_end"], 1) for p in per]
-    return {"decode_trace": summ, "launches": len(per)}
+    return {"decode_trace": summ, "launches": len(per), "workload": args.decode_trace_workload}
 
 
 def extras(pa, runner, W, torch, groups=EXTRA_GROUPS):
