@@ -366,14 +366,13 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
         }
       }
   };
-  // Probabilities of tile kt and O^T += V^T P^T, with the next tile's S^T
-  // (from its K operands ka_next, read earlier) issued among the
-  // exponentials.  The V operands are read and masked first, so that the
-  // masking branch does not split the MFMAs from the exponentials.
-  auto probs_pv = [&](int kt, const f32x16_t& sc, const char* sb, f32x16_t& s_next,
+  // Probabilities of tile kt and O^T += V^T P^T (V operands va, read and
+  // masked by the caller before the tile maximum, so that their LDS latency
+  // passes under it and the masking branch does not split the MFMAs from
+  // the exponentials), with the next tile's S^T (from its K operands
+  // ka_next, read earlier) issued among the exponentials.
+  auto probs_pv = [&](const f32x16_t& sc, const uint4 (&va)[4][2], f32x16_t& s_next,
                       const uint4 (&ka_next)[8]) __attribute__((always_inline)) {
-      uint4 va[4][2];
-      v_operands(kt, sb, va);
       s_next = qk_mfma(ka_next);
       float p[16];
       const float mc = m_run * c;
@@ -394,13 +393,17 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
         l_run = dot2_bf16(pb[ks].z, kOnes, l_run);
         l_run = dot2_bf16(pb[ks].w, kOnes, l_run);
       }
-      // each of the next tile's eight S^T MFMAs followed by six vector
-      // instructions of this tile, so that the matrix cores work under this
-      // wave's own softmax
+      // twelve MFMAs (the next tile's eight S^T, then the first key slice's
+      // four PV) each followed by a few vector or transcendental
+      // instructions of this tile (the exponentials count: mask 0x002 alone
+      // leaves them out), so that the matrix cores work under this wave's
+      // own softmax.  Five per MFMA for a bf16 cache, four for fp8 (measured
+      // best of 4-6 on the mixed batch).
+      constexpr int kValuPerMfma = DIRECT ? 5 : 4;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
+      for (int r = 0; r < 12; ++r) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
+        __builtin_amdgcn_sched_group_barrier(0x402, kValuPerMfma, 1);
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
@@ -445,9 +448,11 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
     {                                                                                                  \
       f32x16_t s_nxt;                                                                                  \
       uint4 ka_n[8];                                                                                   \
-      read_k(NXT, ka_n);                 /* next tile's K operands: their latency under the max */     \
+      uint4 va[4][2];                                                                                  \
+      read_k(NXT, ka_n);                 /* next tile's K and this tile's V operands: their latency */ \
+      v_operands((KT_), CUR, va);        /* under the tile maximum */                                 \
       mask_rescale((KT_), s_cur);                                                                      \
-      probs_pv((KT_), s_cur, CUR, s_nxt, ka_n);                                                        \
+      probs_pv(s_cur, va, s_nxt, ka_n);                                                                \
       s_cur = s_nxt;                                                                                   \
     }
     for (int kt = 0; kt < n_tiles_wg; kt += 4) {
@@ -486,9 +491,11 @@ __global__ void __launch_bounds__(kPrefillWaves * 64, 2) prefill_kernel(PrefillA
   {                                                                                                   \
     f32x16_t s_nxt;                                                                                   \
     uint4 ka_n[8];                                                                                    \
+    uint4 va[4][2];                                                                                   \
     read_k(NXT, ka_n);                                                                                \
+    v_operands((KT_), CUR, va);                                                                       \
     mask_rescale((KT_), s_cur);                                                                       \
-    probs_pv((KT_), s_cur, CUR, s_nxt, ka_n);                                                         \
+    probs_pv(s_cur, va, s_nxt, ka_n);                                                                 \
     s_cur = s_nxt;                                                                                    \
   }                                                                                                   \
   PA_STAGE_STORE(ST, SBUF);                                  /* tile KT_ + 2 */                        \
