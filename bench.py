@@ -32,8 +32,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0       # published dense bf16 matrix peak
 # and WRITE_SIZE passes scaled by the same counters on a plain 1 GiB copy
 # (bench.py --copy-probe 1024), and the hash of the kernel sources they were
 # taken on: once those sources change the figure no longer applies.
-DECODE_TRAFFIC = {"sources_sha256": "cde09573bb0a6ddda467d464ddb4e12705df8ad10e3336f492a1fbd0cdf33319",
-                  "bytes_per_launch": 305806926}
+DECODE_TRAFFIC = {"sources_sha256": "93848a327a0766a70aa4583195624dbfb34fabdaeb74cf349ce2efb820dd305f",
+                  "bytes_per_launch": 305695669}
 DECODE_SOURCES = ("decode_kernel.h", "pa_device.h", "pa_internal.h", "decode_bf16.hip")
 
 
