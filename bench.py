@@ -299,6 +299,20 @@ def extras(pa, runner, W, torch, groups=EXTRA_GROUPS):
                                 TFLOPs=round(fl / med / 1e9, 1), ms=round(med, 4), p10_ms=round(p10, 4),
                                 p90_ms=round(p90, 4), kv_bytes=byt, tokens=int(np.sum(tl)))
         del g
+        torch.cuda.empty_cache()
+        # the same verification over the long-context prefixes (contexts of
+        # 128..32768 tokens: the launch cuts the batch into equal stretches)
+        b = W.verify_long_batch()
+        g = runner.prepare(b)
+        runner.store_step(g)
+        med, p10, p90 = timed_calls(lambda: runner.chunk_step(g), 20)
+        tl = g.chunk["host_prefix"] + g.chunk["host_q"]
+        byt = kv_bytes(tl, b.num_kv_heads, b.head_dim, 2)
+        out["verify_long_context_k4"] = dict(GBps=round(byt / med / 1e6, 1), frac=round(byt / med / 1e6 / HBM_PEAK_GBS, 4),
+                                             ms=round(med, 4), p10_ms=round(p10, 4), p90_ms=round(p90, 4),
+                                             kv_bytes=byt, tokens=int(np.sum(tl)))
+        del g
+        torch.cuda.empty_cache()
     if "handoff" in groups:
         # prefill -> decode KV hand-off of the Qwen3-8B layer's 32 sequences:
         # pack out of the paged pools, store into another cache's own blocks

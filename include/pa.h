@@ -247,12 +247,29 @@ int pa_decode_time_next(void* start_event, void* stop_event);
  * Chunks of at most 32 / (num_q_heads / num_kv_heads) tokens -- the shape of
  * speculative-decoding verification, k draft tokens plus one -- run on a
  * kernel whose matrix-core columns are the (query head, token) pairs of a
- * kv head (serving-stack page, speculative decoding). */
+ * kv head (serving-stack page, speculative decoding).
+ *
+ * workspace (optional, used by that verification kernel only): NULL, or
+ * device memory of at least pa_decode_workspace_bytes() bytes with the same
+ * rules as pa_decode's workspace (zero-filled before its first use; every
+ * completed call leaves it ready for the next; one buffer serves pa_decode
+ * and pa_prefill_chunk calls that run one after another on a stream; calls
+ * that may run at the same time need their own).  Without a workspace, one
+ * workgroup computes each (sequence, kv head) whole, so a batch of unequal
+ * contexts waits for its longest and a batch of few sequences leaves most
+ * CUs idle.  With one, the kernel reads the batch's lengths and, unless every
+ * (sequence, kv head) has a workgroup and none is more than twice an equal
+ * share, cuts the verification keys of the whole batch into equal stretches,
+ * one per CU; a (sequence, kv head) cut between stretches is merged by
+ * log-sum-exp rescaling in the same kernel (at most 4096 sequences; larger
+ * batches run as without).  The results agree within fp32 rounding.  A
+ * non-NULL workspace smaller than pa_decode_workspace_bytes() is rejected
+ * with PA_ERR_WORKSPACE. */
 int pa_prefill_chunk(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* out,
                      int32_t out_dtype, int32_t num_seqs, int32_t num_q_heads, float scale,
                      const int32_t* cu_q_lens, const int32_t* seq_lens, const int32_t* block_table,
                      int32_t max_blocks_per_seq, int32_t max_q_len, int32_t max_seq_len,
-                     void* hip_stream);
+                     void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Checks of index arrays held in HOST memory (no HIP), the same checks that
  * PA_DEBUG_BOUNDS=1 runs on every call's device arrays.  Each returns PA_OK

@@ -47,7 +47,8 @@ SIGNATURES = [
     ("pa_decode", C.c_int, [_CACHE, _P, _I, _P, _I, _I, _I, C.c_float, _P, _I, _P, _I, _I, _P, C.c_size_t, _P]),
     ("pa_decode_noalloc", C.c_int, [_CACHE, _P, _I, _P, _I, _I, _I, C.c_float, _P, _I, _P, _I, _I, _P]),
     ("pa_decode_time_next", C.c_int, [_P, _P]),
-    ("pa_prefill_chunk", C.c_int, [_CACHE, _P, _I, _P, _I, _I, _I, C.c_float, _P, _P, _P, _I, _I, _I, _P]),
+    ("pa_prefill_chunk", C.c_int, [_CACHE, _P, _I, _P, _I, _I, _I, C.c_float, _P, _P, _P, _I, _I, _I, _P,
+                                   C.c_size_t, _P]),
     ("pa_pack_kv", C.c_int, [_CACHE, _P, _I, _P, _P, _I, _I, _P, _P, _P]),
     ("pa_last_error", C.c_char_p, []),
     ("pa_check_slots", C.c_int, [_CACHE, _IP, _I]),

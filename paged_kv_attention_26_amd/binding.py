@@ -221,19 +221,28 @@ def time_next_decode(start: Optional[torch.cuda.Event], stop: Optional[torch.cud
 
 def prefill_chunk(cache: KVCache, q: torch.Tensor, cu_q_lens: torch.Tensor, seq_lens: torch.Tensor,
                   block_table: torch.Tensor, max_q_len: int, max_seq_len: int, scale: float,
-                  out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  split: bool = True, stream=None) -> torch.Tensor:
+    """pa_prefill_chunk.  split: give the verification kernel a workspace
+    (``workspace``, else the stream's default one, shared with decode), so
+    that it cuts the batch's keys into equal stretches; False passes none."""
     T, Hq, D = q.shape
     S = seq_lens.numel()
     if out is None:
         out = torch.empty_like(q)
     if cu_q_lens.numel() != S + 1 or block_table.dim() != 2 or block_table.shape[0] != S:
         raise ValueError("cu_q_lens must be [S+1] and block_table [S, max_blocks]")
+    ws_ptr, ws_bytes = None, 0
+    if split:
+        if workspace is None:
+            workspace = _default_workspace(D, q.device, _stream(stream).value)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel()
     L.check(L.lib().pa_prefill_chunk(C.byref(cache.desc), _dev(q, "q", torch.bfloat16), DTYPE_CODES["bf16"],
                                      _dev(out, "out", torch.bfloat16), DTYPE_CODES["bf16"], S, Hq, float(scale),
                                      _dev(cu_q_lens, "cu_q_lens", torch.int32),
                                      _dev(seq_lens, "seq_lens", torch.int32),
                                      _dev(block_table, "block_table", torch.int32), block_table.shape[1],
-                                     int(max_q_len), int(max_seq_len), _stream(stream)),
+                                     int(max_q_len), int(max_seq_len), ws_ptr, ws_bytes, _stream(stream)),
             "pa_prefill_chunk")
     return out
 

@@ -292,7 +292,8 @@ int pa_decode_trace_next(void* buf) {
 int pa_prefill_chunk(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
                      int32_t num_seqs, int32_t num_q_heads, float scale, const int32_t* cu_q_lens,
                      const int32_t* seq_lens, const int32_t* block_table, int32_t max_blocks_per_seq,
-                     int32_t max_q_len, int32_t max_seq_len, void* hip_stream) {
+                     int32_t max_q_len, int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                     void* hip_stream) {
   int rc = check_cache(cache);
   if (rc) return rc;
   if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
@@ -331,6 +332,16 @@ int pa_prefill_chunk(const pa_kv_cache* cache, const void* q, int32_t q_dtype, v
   a.num_kv_heads = cache->num_kv_heads;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_q_len = max_q_len;
+  a.max_seq_len = max_seq_len;
+  if (workspace) {
+    const pa::DecodeWorkspace lay = pa::decode_workspace_layout(cache->head_dim);
+    if (workspace_bytes < lay.total)
+      return fail(PA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, lay.total);
+    char* ws = static_cast<char*>(workspace);
+    a.arrivals = reinterpret_cast<int32_t*>(ws + lay.arrivals_off);
+    a.part_ml = reinterpret_cast<float*>(ws + lay.ml_off);
+    a.part_acc = reinterpret_cast<float*>(ws + lay.acc_off);
+  }
   const int kv = cache->dtype == PA_BF16 ? pa::KV_BF16 : pa::KV_FP8;
   if (pa::debug_bounds_on()) {
     rc = pa::debug_check_prefill(cache, cu_q_lens, seq_lens, block_table, max_blocks_per_seq, num_seqs, max_q_len,

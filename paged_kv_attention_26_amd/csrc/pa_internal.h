@@ -66,6 +66,11 @@ struct DecodeArgs {
 // Upper bound on the waves one decode launch uses (the workspace is sized for it).
 constexpr int kDecodeMaxWaves = 4096;
 constexpr int kDecodeMaxGroup = 8;
+// Upper bound on the workgroups of a split verify launch: two partials of 32
+// columns each, and one arrival counter, per workgroup in the same workspace.
+constexpr int kVerifyMaxGroups = 1024;
+static_assert(kVerifyMaxGroups * 2 * 32 <= kDecodeMaxWaves * 2 * kDecodeMaxGroup, "verify partial slots");
+static_assert(kVerifyMaxGroups <= kDecodeMaxWaves, "verify arrival counters");
 
 struct PrefillArgs {
   const void* k_cache;
@@ -78,8 +83,16 @@ struct PrefillArgs {
   const int32_t* seq_lens;
   const int32_t* block_table;
   float scale_log2;  // softmax scale * log2(e)
-  int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, max_q_len;
+  int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, max_q_len, max_seq_len;
   int32_t num_qtiles, wg_per_pair;  // filled by the launcher
+  // Verify launches with a workspace (the decode workspace's layout): the
+  // partial results of items split between workgroups, [group][2][32 columns]
+  // (max, sum) and [group][2][32][head_dim], and one arrival counter per item,
+  // keyed by its last workgroup.  part_acc == nullptr: no split.
+  float* part_ml;
+  float* part_acc;
+  int32_t* arrivals;
+  int32_t total_groups;  // filled by the launcher
 };
 
 struct DecodeWorkspace {

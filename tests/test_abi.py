@@ -129,7 +129,7 @@ def test_pack_rejects_bad_arguments():
 def test_prefill_rejects_bad_arguments():
     lib = L.lib()
     c = cache(head_dim=128, num_kv_heads=8)
-    args = [FAKE, L.PA_BF16, FAKE, L.PA_BF16, 2, 32, 0.088, FAKE, FAKE, FAKE, 64, 512, 1024, None]
+    args = [FAKE, L.PA_BF16, FAKE, L.PA_BF16, 2, 32, 0.088, FAKE, FAKE, FAKE, 64, 512, 1024, None, 0, None]
     assert lib.pa_prefill_chunk(None, *args) == L.PA_ERR_NULL
     bad = list(args); bad[5] = 30                                      # Hq % Hkv
     assert lib.pa_prefill_chunk(C.byref(c), *bad) == L.PA_ERR_SHAPE
@@ -137,6 +137,9 @@ def test_prefill_rejects_bad_arguments():
     assert lib.pa_prefill_chunk(C.byref(c), *bad) in (L.PA_ERR_DTYPE, L.PA_ERR_UNSUPPORTED)
     bad = list(args); bad[10] = 8                                      # table narrower than max_seq_len
     assert lib.pa_prefill_chunk(C.byref(c), *bad) in (L.PA_ERR_SHAPE, L.PA_ERR_UNSUPPORTED)
+    need = lib.pa_decode_workspace_bytes(2, 32, 128, 1024, 64)
+    bad = list(args); bad[13] = FAKE; bad[14] = need - 1                 # a workspace, but too small
+    assert lib.pa_prefill_chunk(C.byref(c), *bad) == L.PA_ERR_WORKSPACE
 
 
 def test_workspace_size_query():
@@ -436,5 +439,5 @@ def test_prefill_subset_is_rejected_with_its_code(dtype, d, q_io, code):
     if dtype == L.PA_FP8_E4M3:
         kw.update(k_scale=FAKE, v_scale=FAKE)
     c = cache(**kw)
-    args = [FAKE, q_io, FAKE, q_io, 2, 32, 0.088, FAKE, FAKE, FAKE, 64, 512, 1024, None]
+    args = [FAKE, q_io, FAKE, q_io, 2, 32, 0.088, FAKE, FAKE, FAKE, 64, 512, 1024, None, 0, None]
     assert lib.pa_prefill_chunk(C.byref(c), *args) == code

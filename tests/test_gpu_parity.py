@@ -828,6 +828,89 @@ def test_verify_full_batch():
     assert err < TOL["bf16"]
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_verify_split_and_whole_launches(kv):
+    """Speculative verification in both launch forms: with a workspace (the
+    batch's key tiles cut into equal stretches, one per CU, items cut between
+    stretches merged in the kernel) and without (one workgroup per (sequence,
+    kv head)).  Empty chunks sit between long and short contexts, so
+    stretches start and end inside items, on items of other heads and past
+    sequences without units; both forms against the oracle, and three calls
+    in a row of the split form bit-identical (its counters return to zero)."""
+    from paged_kv_attention_26_amd import binding as pa, runner
+    batch = chunk_batch(f"verify-split-{kv}", [50, 3000, 10, 700, 0, 2500, 9000, 31, 4100],
+                        [5, 0, 5, 3, 8, 0, 1, 5, 2], kv=kv, seed=77)
+    say(f"[gpu] verify split / whole {batch.name}")
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    c = g.chunk
+    ref = OS.chunk_ref(batch, OS.build(batch))
+    call = lambda split: pa.prefill_chunk(g.cache, c["q"], c["cu"], c["seq_lens"], c["table"], c["max_q"],
+                                          c["max_seq"], batch.scale, split=split)
+    whole = out_f64(call(False))
+    outs = [call(True).clone() for _ in range(3)]
+    torch.cuda.synchronize()
+    got = out_f64(outs[0])
+    ew, es = np.max(np.abs(whole - ref)), np.max(np.abs(got - ref))
+    say(f"      max abs err: whole {ew:.3e}, split {es:.3e}")
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(whole))
+    assert ew < TOL[kv] and es < TOL[kv]
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+def test_verify_cut_stretches_over_64_sequences():
+    """A split verification launch over more than 64 sequences (the unit
+    prefix then lives in LDS, built by the whole workgroup): 90 short
+    contexts, some with empty chunks, around two long ones, so the launch cuts
+    the batch into stretches; against the oracle."""
+    from paged_kv_attention_26_amd import runner
+    rng = np.random.default_rng(91)
+    P = rng.integers(0, 300, 92)
+    P[17], P[70] = 12000, 7000
+    q = rng.integers(1, 6, 92)
+    q[[3, 40, 41, 88]] = 0
+    batch = chunk_batch("verify-cut-92", P, q, seed=91)
+    say(f"[gpu] verify {batch.name}")
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    got = out_f64(runner.chunk_step(g))
+    torch.cuda.synchronize()
+    err = np.max(np.abs(got - OS.chunk_ref(batch, OS.build(batch))))
+    say(f"      max abs err {err:.3e}")
+    assert np.all(np.isfinite(got)) and err < TOL["bf16"]
+
+
+def test_verify_long_context_full_launch():
+    """Speculative verification over the long-context prefixes at full size
+    (128 seqs, 713k tokens, contexts up to 28k), as benchmarked: the launch
+    cuts the batch into equal stretches, so the long contexts are merged from
+    several workgroups.  Every output is finite; every third sequence and the
+    16 longest against the oracle."""
+    from oracle import paged
+    from paged_kv_attention_26_amd import runner
+    say("[gpu] verify long context full")
+    batch = W.verify_long_batch()
+    g = runner.prepare(batch)
+    runner.store_step(g)
+    got = out_f64(runner.chunk_step(g))
+    torch.cuda.synchronize()
+    del g
+    assert np.all(np.isfinite(got))
+    st = OS.build(batch)
+    lens = batch.total_lens
+    q_lens = batch.new_lens
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
+    sel = sorted(set(range(0, len(lens), 3)) | set(np.argsort(lens)[-16:].tolist()))
+    tables = OS.table_array([st.tables[i] for i in sel], st.pad_block)
+    qs = np.concatenate([batch.q_chunk[cu[i]:cu[i + 1]] for i in sel])
+    rows = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in sel])
+    cu_sel = np.concatenate([[0], np.cumsum(q_lens[sel])]).astype(np.int64)
+    ref = paged.prefill_chunk_attention(st.kc, st.vc, "bf16", qs, "bf16", cu_sel, lens[sel], tables, batch.scale)
+    err = np.max(np.abs(got[rows] - ref))
+    say(f"      {len(sel)} sequences (L up to {int(lens.max())}): max abs err {err:.3e}")
+    assert err < TOL["bf16"]
+
+
 def test_debug_bounds_mode(monkeypatch):
     """PA_DEBUG_BOUNDS=1: every call first checks the values in its device
     index arrays on the host.  Valid calls give the same bits as without the

@@ -282,6 +282,20 @@ def verify_batch(small=False, draft=4) -> PagedBatch:
                        rng=rng)
 
 
+def verify_long_batch(draft=4, n=None) -> PagedBatch:
+    """Speculative verification over the long-context config's prefixes: its
+    128 context lengths (log-uniform 128..32768, the first draw) as accepted
+    prefixes, each appending a chunk of draft + 1 tokens, Qwen3-8B heads,
+    bf16, B 16, pool 1.25x (seed 7).  ``n``: only the first n sequences."""
+    lens = config3_lengths()
+    if n is not None:
+        lens = lens[:n]
+    rng = np.random.default_rng(7)
+    return paged_batch("long-context-verify", 7, kv_dtype="bf16", io_dtype="bf16", Hq=32, Hkv=8, d=128, B=16,
+                       prior_lens=lens, new_lens=np.full(len(lens), draft + 1, np.int64),
+                       is_chunk=np.ones(len(lens), bool), rng=rng)
+
+
 def config5(small=False, literal_fork=False) -> ForkBatch:
     """CoW fork with fp8 KV: a 2048-token prompt plus the parent's first generated
     token (2049 shared tokens, so the tail block is partly filled and shared)
