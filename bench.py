@@ -32,8 +32,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0       # published dense bf16 matrix peak
 # and WRITE_SIZE passes scaled by the same counters on a plain 1 GiB copy
 # (bench.py --copy-probe 1024), and the hash of the kernel sources they were
 # taken on: once those sources change the figure no longer applies.
-DECODE_TRAFFIC = {"sources_sha256": "93848a327a0766a70aa4583195624dbfb34fabdaeb74cf349ce2efb820dd305f",
-                  "bytes_per_launch": 305695669}
+DECODE_TRAFFIC = {"sources_sha256": "d01a4e3d611ecc03663c3771cbe1e30259d1e6ec6ff9cb4ca5142d99ebb2c3bb",
+                  "bytes_per_launch": 305728183}
 DECODE_SOURCES = ("decode_kernel.h", "pa_device.h", "pa_internal.h", "decode_bf16.hip")
 
 
