@@ -114,8 +114,24 @@ __global__ void __launch_bounds__(kVerifyThreads) verify_kernel(PrefillArgs a,
   const char* vpool = static_cast<const char*>(a.v_cache);
   using Raw = KvRaw<KV>;
   constexpr int ES = Raw::ES;                   // cache element bytes
+  // Per-sequence lengths.  For batches of at most 64 sequences lane i loads
+  // sequence i's once, and any sequence's are then a register read by lane
+  // (no memory round trip in the wave's chain of dependent steps); larger
+  // batches read memory (through the scalar cache).
+  const bool lane_meta = S <= 64;
+  int m_q0 = 0, m_ql = 0, m_kend = 0;
+  if (lane_meta && lane < S) {
+    m_q0 = cu_q_lens[lane];
+    m_ql = cu_q_lens[lane + 1] - m_q0;
+    m_kend = seq_lens[lane];
+  }
+  const int m_tiles = m_ql > 0 ? (max(m_kend, 0) + KT - 1) / KT : 0;
+  auto q0_of = [&](int s) { return lane_meta ? __builtin_amdgcn_readlane(m_q0, s) : cu_q_lens[s]; };
+  auto qlen_of = [&](int s) { return lane_meta ? __builtin_amdgcn_readlane(m_ql, s) : cu_q_lens[s + 1] - cu_q_lens[s]; };
+  auto kend_of = [&](int s) { return lane_meta ? __builtin_amdgcn_readlane(m_kend, s) : seq_lens[s]; };
   // tiles of a sequence's items (none when its chunk is empty)
   auto tiles_of = [&](int s) {
+    if (lane_meta) return __builtin_amdgcn_readlane(m_tiles, s);
     return cu_q_lens[s + 1] > cu_q_lens[s] ? (max(seq_lens[s], 0) + KT - 1) / KT : 0;
   };
 
@@ -128,7 +144,7 @@ __global__ void __launch_bounds__(kVerifyThreads) verify_kernel(PrefillArgs a,
   const bool wave_prefix = S <= 64;
   int l_tiles = 0, l_excl = 0;
   if (split && wave_prefix) {
-    l_tiles = lane < S ? tiles_of(lane) : 0;
+    l_tiles = m_tiles;
     int x = l_tiles * Hkv, mx = l_tiles;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -245,7 +261,7 @@ __global__ void __launch_bounds__(kVerifyThreads) verify_kernel(PrefillArgs a,
     s.tile0 = 0;
     s.useg = us;
     s.t1 = seg_end(s.seq, 0, us);
-    s.kend = seq_lens[s.seq];
+    s.kend = kend_of(s.seq);
     return true;
   };
   // this wave's first tile in s's segment, or in the first later one where it has one
@@ -281,7 +297,7 @@ __global__ void __launch_bounds__(kVerifyThreads) verify_kernel(PrefillArgs a,
   // ---- Q^T of a slot's item as 8 B operands (k = 16 head dims each): row q0 + t, dims 16s + 8hh .. + 7
   uint4 qb[8];
   auto load_q = [&](const Slot& s) __attribute__((always_inline)) {
-    const int q0 = cu_q_lens[s.seq], ql = cu_q_lens[s.seq + 1] - q0;
+    const int q0 = q0_of(s.seq), ql = qlen_of(s.seq);
     const int row = q0 + min(t, ql - 1);
     const uint16_t* qr = static_cast<const uint16_t*>(a.q) + (size_t(row) * Hq + s.kvh * G + gq) * D + 8 * hh;
 #pragma unroll
@@ -321,7 +337,7 @@ __global__ void __launch_bounds__(kVerifyThreads) verify_kernel(PrefillArgs a,
 
   // cs walks the stretch's segments; cl is the slot whose tile is in ka / va
   // (landed or in flight), ci the slot after it, whose block ids are in id0 / id1
-  Slot cs{u, 0, seq, kvh, tile0, 0, 0, seq_lens[seq], true};
+  Slot cs{u, 0, seq, kvh, tile0, 0, 0, kend_of(seq), true};
   cs.t1 = seg_end(seq, tile0, u);
   Slot cl = cs;
   settle(cl);
@@ -346,8 +362,8 @@ __global__ void __launch_bounds__(kVerifyThreads) verify_kernel(PrefillArgs a,
   int seq0 = 0, kvh0 = 0, seq1 = 0, kvh1 = 0;
   int64_t first0 = 0, first1 = 0;
   for (;;) {                                                // segment cs.k of the stretch
-    const int q0 = cu_q_lens[cs.seq];
-    const int q_len = cu_q_lens[cs.seq + 1] - q0;
+    const int q0 = q0_of(cs.seq);
+    const int q_len = qlen_of(cs.seq);
     const int key_end = cs.kend;                            // keys 0 .. key_end - 1 (prefix and chunk)
     const int P = key_end - q_len;
     const int n_tiles = (key_end + KT - 1) / KT;
@@ -557,7 +573,7 @@ __global__ void __launch_bounds__(kVerifyThreads) verify_kernel(PrefillArgs a,
       const int sq = it ? seq1 : seq0, kh = it ? kvh1 : kvh0;
       const int cnt = s_merge[3 + it];
       const int slot0 = (s_merge[2] >> it) & 1;
-      const int q0 = cu_q_lens[sq], q_len = cu_q_lens[sq + 1] - q0;
+      const int q0 = q0_of(sq), q_len = qlen_of(sq);
       if (ct >= q_len) continue;
       const float c = KV == KV_FP8 ? a.scale_log2 * a.k_scale[kh] : a.scale_log2;
       const float v_mul = KV == KV_FP8 ? a.v_scale[kh] : 1.f;
