@@ -1,7 +1,8 @@
 """Benchmark of the paged-attention hot path on one MI355X.
 
-A step is one pass of the path over one batch: pa_store_kv of the step's new
-tokens, then the attention call(s).  The default workload is one Qwen3-8B
+A step is one pass of the path over one batch: the store of the step's new
+tokens and the attention, by default in one pa_decode_append launch
+(``--separate-store``: pa_store_kv, then pa_decode).  The default workload is one Qwen3-8B
 attention layer in decode: 32 sequences with contexts uniform in
 [512, 4096], 32 query / 8 KV heads, head_dim 128, bf16, block size 16.  To
 keep the 256 MB last-level cache from serving the KV, each step uses the
@@ -28,13 +29,14 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0       # published dense bf16 matrix peak
 
 
-# HBM bytes per decode_kernel launch on this workload, from rocprofv3 FETCH_SIZE
+# HBM bytes per decode_kernel launch on this workload (the launch that also
+# stores the step's tokens, pa_decode_append), from rocprofv3 FETCH_SIZE
 # and WRITE_SIZE passes scaled by the same counters on a plain 1 GiB copy
 # (bench.py --copy-probe 1024), and the hash of the kernel sources they were
 # taken on: once those sources change the figure no longer applies.
-DECODE_TRAFFIC = {"sources_sha256": "d01a4e3d611ecc03663c3771cbe1e30259d1e6ec6ff9cb4ca5142d99ebb2c3bb",
-                  "bytes_per_launch": 305728183}
-DECODE_SOURCES = ("decode_kernel.h", "pa_device.h", "pa_internal.h", "decode_bf16.hip")
+DECODE_TRAFFIC = {"sources_sha256": "7297795b754726b56dfe567c0d711b70b90a3e79e05573a955dd0a97ea559105",
+                  "bytes_per_launch": 307067887}
+DECODE_SOURCES = ("decode_kernel.h", "store_row.h", "pa_device.h", "pa_internal.h", "decode_bf16.hip")
 
 
 def decode_sources_sha256():
@@ -69,6 +71,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=8, help="distinct layer caches cycled through")
     ap.add_argument("--partition", type=int, default=64, help="split-K partition tokens (0 = no split)")
+    ap.add_argument("--separate-store", action="store_true",
+                    help="store the new tokens with pa_store_kv before pa_decode instead of in the decode launch")
     ap.add_argument("--stamp-every", type=int, default=4,
                     help="time every N-th decode launch of the timed region with kernel-stamped events")
     ap.add_argument("--no-extras", action="store_true", help="skip the secondary measurements")
@@ -614,10 +618,20 @@ def main():
     ws = pa.decode_workspace(len(d0["idx"]), base.num_q_heads, base.head_dim, d0["max_len"], args.partition)
     out = torch.empty_like(d0["q"])
     step_bytes = kv_bytes(lens_all, base.num_kv_heads, base.head_dim, 2)
+    fused = not args.separate_store
+    # the decode launch's own algorithmic bytes: the KV it reads, and when it
+    # also stores the step's tokens, their rows read once and written once
+    new_rows = len(lens_all) * base.num_kv_heads * base.head_dim * 2 * 2
+    launch_bytes = step_bytes + (2 * new_rows if fused else 0)
 
-    def step(i):
+    def step(i, stamp=None):
         g = layers[i % len(layers)]
-        runner.store_step(g)
+        if not fused:
+            runner.store_step(g)
+        if stamp is not None:
+            pa.time_next_decode(*stamp)
+        if fused:
+            return runner.decode_step_append(g, out=out, partition_tokens=args.partition, workspace=ws)
         return runner.decode_step(g, out=out, partition_tokens=args.partition, workspace=ws)
 
     for i in range(args.warmup):
@@ -637,18 +651,14 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        g = layers[i % len(layers)]
-        runner.store_step(g)
-        if i in evs:
-            pa.time_next_decode(evs[i][0], evs[i][1])
-        runner.decode_step(g, out=out, partition_tokens=args.partition, workspace=ws)
+        step(i, evs.get(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dec_ms = np.array([a.elapsed_time(b) for a, b in evs.values()])
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_avg = float(dec_ms.mean())
-    achieved = step_bytes / (dec_avg * 1e-3) / 1e9
+    achieved = launch_bytes / (dec_avg * 1e-3) / 1e9
     rec = {
         "metric": "paged decode KV GB/s (% HBM peak) + prefill-chunk TFLOP/s, Qwen3-8B layer",
         "value": round(value, 1),
@@ -663,19 +673,20 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "qwen3-8b decode layer: 32 seqs, ctx U[512,4096], Hq 32 / Hkv 8, d 128, "
-                               "bf16 KV, block 16, store 32 tokens + paged decode",
+                               "bf16 KV, block 16, 32 new tokens stored + paged decode"
+                               + (" in one launch" if fused else " (separate store launch)"),
                    "global_batch": int(len(lens_all)), "seq_len": int(np.max(lens_all)),
                    "kv_tokens": int(np.sum(lens_all)), "layer_caches": args.layers,
                    "partition_tokens": args.partition, "parallelism": "single-gpu"},
         "device": device_info(torch),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": decode_traffic(),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": decode_traffic() if fused else None,
                      "kernel": "pa::decode_kernel<bf16, d128, B16, G4>",
                      "kernel_ms_avg": round(dec_avg, 5), "kernel_ms_median": round(float(np.median(dec_ms)), 5),
                      "kernel_ms_p10": round(float(np.percentile(dec_ms, 10)), 5),
                      "kernel_ms_p90": round(float(np.percentile(dec_ms, 90)), 5),
                      "kernel_launches_timed": int(len(dec_ms)),
-                     "algorithmic_bytes_per_launch": step_bytes},
+                     "algorithmic_bytes_per_launch": launch_bytes},
     }
     if not args.no_extras:
         del layers

@@ -193,6 +193,30 @@ int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* ou
               int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
               int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* A decode step's store and attention in one launch (nanoPD page: the paged
+ * KV cache's store operation beside its attention kernel; serving-stack page,
+ * section 2.3: a sequence's new token goes to offset length % block_size of
+ * its last block): the same results, bit for bit, as
+ *   pa_store_kv(k_new, v_new, slots) followed by pa_decode(...)
+ * where token s of the store is sequence s's new token, at position
+ * context_lens[s] - 1, in the slot the block table gives for that position:
+ *   slot = block_table[s][(L-1) / block_size] * block_size + (L-1) % block_size.
+ *
+ *   k_new, v_new : [num_seqs][num_kv_heads][head_dim] device rows in the
+ *                  cache's input dtype (F32 for an F32 cache, BF16 for BF16
+ *                  and FP8 caches; an FP8 cache stores value / scale[h]
+ *                  rounded to e4m3, as pa_store_kv does).
+ * Sequences with context_lens[s] == 0 store nothing.  All other arguments,
+ * the workspace rules and the errors are those of pa_decode; NULL k_new or
+ * v_new is PA_ERR_NULL.  The block of the new token must be allocated in the
+ * table (as for pa_store_kv).  pa_decode_time_next arms this call as it arms
+ * pa_decode. */
+int pa_decode_append(const pa_kv_cache* cache, const void* k_new, const void* v_new, const void* q,
+                     int32_t q_dtype, void* out, int32_t out_dtype, int32_t num_seqs, int32_t num_q_heads,
+                     float scale, const int32_t* block_table, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t max_context_len, int32_t partition_tokens,
+                     void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* pa_decode without a caller workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, serving loops or harnesses
  * that forbid allocation).  Arguments, results and errors as for pa_decode.
@@ -217,7 +241,7 @@ int pa_decode_noalloc(const pa_kv_cache* cache, const void* q, int32_t q_dtype, 
  * NULL) with its kernel's own start and end timestamps, through
  * hipExtLaunchKernel, instead of marker packets placed around the call in the
  * stream, which add several microseconds of their own to the window and to
- * the stream.  One call arms one pa_decode call: that call disarms it at
+ * the stream.  One call arms one pa_decode (or pa_decode_append) call: that call disarms it at
  * entry, whether it then launches or not (a call rejected by its checks, or
  * one with num_seqs == 0, leaves the events untouched).  Passing NULL, NULL
  * disarms.  Returns PA_OK. */

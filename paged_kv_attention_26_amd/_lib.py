@@ -46,6 +46,8 @@ SIGNATURES = [
     ("pa_decode_workspace_bytes", C.c_size_t, [_I, _I, _I, _I, _I]),
     ("pa_decode", C.c_int, [_CACHE, _P, _I, _P, _I, _I, _I, C.c_float, _P, _I, _P, _I, _I, _P, C.c_size_t, _P]),
     ("pa_decode_noalloc", C.c_int, [_CACHE, _P, _I, _P, _I, _I, _I, C.c_float, _P, _I, _P, _I, _I, _P]),
+    ("pa_decode_append", C.c_int, [_CACHE, _P, _P, _P, _I, _P, _I, _I, _I, C.c_float, _P, _I, _P, _I, _I, _P,
+                                   C.c_size_t, _P]),
     ("pa_decode_time_next", C.c_int, [_P, _P]),
     ("pa_prefill_chunk", C.c_int, [_CACHE, _P, _I, _P, _I, _I, _I, C.c_float, _P, _P, _P, _I, _I, _I, _P,
                                    C.c_size_t, _P]),

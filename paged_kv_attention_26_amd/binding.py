@@ -181,6 +181,36 @@ def decode(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor, context_l
     return out
 
 
+def decode_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                  block_table: torch.Tensor, context_lens: torch.Tensor, max_context_len: int, scale: float,
+                  out: Optional[torch.Tensor] = None, partition_tokens: int = 64,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pa_decode_append: store each sequence's new token (k_new / v_new rows
+    [S, Hkv, d], at position context_lens[s] - 1) and decode, in one launch;
+    the same results as store_kv followed by decode."""
+    S, Hq, D = q.shape
+    if D != cache.head_dim:
+        raise ValueError("q head_dim does not match the cache")
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = _default_workspace(D, q.device, _stream(stream).value)
+    if block_table.dim() != 2 or block_table.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_table must be [S, max_blocks] and context_lens [S]")
+    if tuple(k_new.shape) != (S, cache.num_kv_heads, D) or tuple(v_new.shape) != (S, cache.num_kv_heads, D):
+        raise ValueError("k_new / v_new must be [S, num_kv_heads, head_dim]")
+    io = DTYPE_CODES["f32"] if cache.dtype == "f32" else DTYPE_CODES["bf16"]
+    L.check(L.lib().pa_decode_append(C.byref(cache.desc), _dev(k_new, "k_new", cache.io_dtype),
+                                     _dev(v_new, "v_new", cache.io_dtype), _dev(q, "q", cache.io_dtype), io,
+                                     _dev(out, "out", cache.io_dtype), io, S, Hq, float(scale),
+                                     _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+                                     _dev(context_lens, "context_lens", torch.int32), int(max_context_len),
+                                     int(partition_tokens), _dev(workspace, "workspace"), workspace.numel(),
+                                     _stream(stream)),
+            "pa_decode_append")
+    return out
+
+
 def decode_noalloc(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor, context_lens: torch.Tensor,
                    max_context_len: int, scale: float, out: Optional[torch.Tensor] = None,
                    partition_tokens: int = 64, stream=None) -> torch.Tensor:

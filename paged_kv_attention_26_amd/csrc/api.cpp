@@ -201,10 +201,17 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   return pa::decode_workspace_layout(head_dim).total;
 }
 
-int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
-              int32_t num_seqs, int32_t num_q_heads, float scale, const int32_t* block_table,
-              int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
-              int32_t partition_tokens, void* workspace, size_t workspace_bytes_given, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// pa_decode, and pa_decode_append (append: the new rows k_new / v_new are
+// stored first; name: the entry point, for messages).
+int decode_call(const char* name, bool append, const pa_kv_cache* cache, const void* k_new, const void* v_new, const void* q,
+                int32_t q_dtype, void* out, int32_t out_dtype, int32_t num_seqs, int32_t num_q_heads, float scale,
+                const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                int32_t max_context_len, int32_t partition_tokens, void* workspace, size_t workspace_bytes_given,
+                void* hip_stream) {
   const pa::LaunchEvents ev = g_decode_events;             // armed for this call only
   g_decode_events = pa::LaunchEvents{};
   int rc = check_cache(cache);
@@ -230,11 +237,14 @@ int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* ou
   if (num_seqs == 0) return PA_OK;
   if (!q || !out || !block_table || !context_lens || !workspace)
     return fail(PA_ERR_NULL, "q / out / block_table / context_lens / workspace is NULL");
+  if (append && (!k_new || !v_new)) return fail(PA_ERR_NULL, "%s: k_new / v_new is NULL", name);
   const pa::DecodeWorkspace lay = pa::decode_workspace_layout(cache->head_dim);
   if (workspace_bytes_given < lay.total)
     return fail(PA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes_given, lay.total);
   char* ws = static_cast<char*>(workspace);
   pa::DecodeArgs a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.k_cache = cache->k_cache;
   a.v_cache = cache->v_cache;
   a.k_scale = cache->k_scale;
@@ -267,9 +277,32 @@ int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* ou
   hipError_t e = pa::launch_decode(a, kv, cache->head_dim, cache->block_size, G, upper_units,
                                    static_cast<hipStream_t>(hip_stream), ev);
   if (e == hipErrorInvalidValue) return fail(PA_ERR_UNSUPPORTED, "no decode kernel for this shape");
-  if (e != hipSuccess) return hip_fail(e, "pa_decode launch");
+  if (e != hipSuccess) return hip_fail(e, name);
   g_err[0] = 0;
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode(const pa_kv_cache* cache, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
+              int32_t num_seqs, int32_t num_q_heads, float scale, const int32_t* block_table,
+              int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+              int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return decode_call("pa_decode", false, cache, nullptr, nullptr, q, q_dtype, out, out_dtype, num_seqs, num_q_heads, scale,
+                     block_table, max_blocks_per_seq, context_lens, max_context_len, partition_tokens, workspace,
+                     workspace_bytes, hip_stream);
+}
+
+int pa_decode_append(const pa_kv_cache* cache, const void* k_new, const void* v_new, const void* q, int32_t q_dtype,
+                     void* out, int32_t out_dtype, int32_t num_seqs, int32_t num_q_heads, float scale,
+                     const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                     int32_t max_context_len, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                     void* hip_stream) {
+  return decode_call("pa_decode_append", true, cache, k_new, v_new, q, q_dtype, out, out_dtype, num_seqs, num_q_heads,
+                     scale, block_table, max_blocks_per_seq, context_lens, max_context_len, partition_tokens,
+                     workspace, workspace_bytes, hip_stream);
 }
 
 int pa_decode_time_next(void* start_event, void* stop_event) {

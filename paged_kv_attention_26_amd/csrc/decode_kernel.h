@@ -57,6 +57,7 @@
 
 #include "pa_device.h"
 #include "pa_internal.h"
+#include "store_row.h"
 
 #ifndef PA_DECODE_STEP_TOKENS
 #define PA_DECODE_STEP_TOKENS 64
@@ -486,7 +487,48 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
   int ids_nx[C::BPC];
   cursor_ids(nx, ids_nx);
   int kvh_nx = nx.kvh;
+  // Append: partitions are whole blocks, so the last block of a (sequence,
+  // kv head), which receives the step's new token (position length - 1), is
+  // read by one wave only, the one whose range holds the item's last
+  // partition; that wave stores the token.  The first such item's rows are
+  // fetched with the query, so the two share one wait.  The stores then go
+  // out ahead of every tile load of the wave, and vector memory operations
+  // complete in issue order, so each later step, whose loads are issued after
+  // the wait for an earlier step's tiles, sees them; only a first step that
+  // holds a stored token waits for the stores themselves.
+  auto append_item = [&](int& sq, int& kh, int64_t& base) -> bool {   // next item to store, from (sq, kh)
+    for (;;) {
+      const int L = len_of(sq);
+      const int nu = units_of(L, PT);
+      if (base + nu > u_end) return false;                // its last partition lies past this range
+      if (L > 0) return true;
+      base += nu;
+      if (base >= u_end) return false;
+      if (++kh == Hkv) {
+        kh = 0;
+        ++sq;
+      }
+    }
+  };
+  constexpr int IN_ES = KV == KV_F32 ? 4 : 2;             // element bytes of k_new / v_new
+  auto new_row = [&](int sq, int kh) {
+    const size_t r = (size_t(sq) * Hkv + kh) * D * IN_ES;
+    return load_new_row<KV>(static_cast<const char*>(a.k_new) + r, static_cast<const char*>(a.v_new) + r, D);
+  };
+  auto new_slot = [&](int sq) {                            // slot of position length - 1
+    const int L = len_of(sq);
+    return uniform(block_table[size_t(sq) * a.max_blocks_per_seq + (L - 1) / B]) * B + (L - 1) % B;
+  };
+  int ap_sq = seq, ap_kh = kvh;
+  int64_t ap_base = u - part;                             // first unit of (ap_sq, ap_kh)
+  const bool ap = a.k_new != nullptr && append_item(ap_sq, ap_kh, ap_base);
   load_q(qf, qp, seq, kvh);
+  NewRow ap_row{};
+  int ap_slot = -1;
+  if (ap) {
+    ap_row = new_row(ap_sq, ap_kh);
+    ap_slot = new_slot(ap_sq);
+  }
 #ifdef PA_DECODE_TRACE
   __builtin_amdgcn_s_waitcnt(0xC07F);                       // lgkmcnt(0): the block ids are in
   PA_TRACE_STAMP(tr_ids);
@@ -496,6 +538,30 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, const int32_t
   // in-flight tile (vmcnt(0)) at each step.
   __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0) only
   __builtin_amdgcn_sched_barrier(0);
+  if (ap) {
+    for (;;) {
+      float ksc = 1.f, vsc = 1.f;
+      if constexpr (KV == KV_FP8) {
+        ksc = a.k_scale[ap_kh];
+        vsc = a.v_scale[ap_kh];
+      }
+      store_new_row<KV>(ap_row, const_cast<void*>(a.k_cache), const_cast<void*>(a.v_cache), ap_slot, ap_kh, Hkv, D,
+                        B, ksc, vsc);
+      ap_base += units_of(len_of(ap_sq), PT);
+      if (ap_base >= u_end) break;
+      if (++ap_kh == Hkv) {
+        ap_kh = 0;
+        ++ap_sq;
+      }
+      if (!append_item(ap_sq, ap_kh, ap_base)) break;
+      ap_row = new_row(ap_sq, ap_kh);
+      ap_slot = new_slot(ap_sq);
+    }
+    // the first step holds the last block of an item stored above
+    if (nx.live && nx.p_end == units_of(len_of(nx.seq), PT) && nx.blk + C::BPC > nx.last_blk)
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   load_k(ids_nx, kvh_nx);                                   // keys before values, as in the loop
   __builtin_amdgcn_sched_barrier(0);
   load_v(ids_nx, kvh_nx);

@@ -58,6 +58,11 @@ struct DecodeArgs {
   float scale_log2;   // softmax scale * log2(e)
   int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq;
   int32_t part_tokens, total_waves;  // total_waves is set by the launcher
+  // the step's new token of each (sequence, kv head), [num_seqs][Hkv][head_dim]
+  // in the cache's input dtype, stored at position context_len - 1 before
+  // the attention reads it; null: nothing is stored
+  const void* k_new;
+  const void* v_new;
   // [total_waves][16] per-wave time stamps, written only by kernels built
   // with PA_DECODE_TRACE (a measurement build); null otherwise
   uint32_t* trace;

@@ -12,6 +12,7 @@
 // it (nanoPD page, paged KV cache with CoW; serving-stack page 2.3, cow()).
 #include "pa_device.h"
 #include "pa_internal.h"
+#include "store_row.h"
 
 namespace pa {
 
@@ -226,71 +227,22 @@ constexpr int kStoreRowsMaxTokens = 128;
 // The store of a few scattered tokens (a decode step: one new token per
 // sequence), where the time is latency, not bandwidth.  One wave per (token,
 // kv head), so a 32-token step spreads over 256 waves instead of eight
-// workgroups.  Every load of the wave (its slot, fp8 scales, its key row as
-// 16-byte chunks, its value row one element per lane) is issued before any store,
-// so the wave pays one memory round trip; then the key row goes out as
-// 16-byte chunks and the value elements go to their transposed places
-// (head dim d at element d * block_size + offset of the tile).
+// workgroups (the wave's work is store_row).
 template <int KV>
 __global__ void __launch_bounds__(256) store_rows_kernel(StoreArgs a) {
-  constexpr int IN_ES = (KV == KV_F32) ? 4 : (KV == KV_FP8_RAW ? 1 : 2);   // input element bytes
-  constexpr int OUT_ES = (KV == KV_F32) ? 4 : (KV == KV_BF16 ? 2 : 1);
-  constexpr int EPC = 16 / IN_ES;                          // input elements per 16-byte chunk
-  const int H = a.num_kv_heads, D = a.head_dim, BS = a.block_size;
+  const int H = a.num_kv_heads, D = a.head_dim;
   const int64_t pair = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (pair >= int64_t(a.num_tokens) * H) return;           // no barrier in this kernel
   const int t = int(pair / H), h = int(pair - int64_t(t) * H);
-  const int lane = threadIdx.x & 63;
-  const int cpr = D / EPC;                                 // key chunks per row (<= 32)
-  const int vpl = D / 64;                                  // value elements per lane (1 or 2)
+  constexpr int IN_ES = (KV == KV_F32) ? 4 : (KV == KV_FP8_RAW ? 1 : 2);   // input element bytes
   const char* krow = static_cast<const char*>(a.k_new) + (size_t(t) * H + h) * D * IN_ES;
   const char* vrow = static_cast<const char*>(a.v_new) + (size_t(t) * H + h) * D * IN_ES;
-
-  const int slot = a.slot_mapping[t];
   float ksc = 1.f, vsc = 1.f;
   if constexpr (KV == KV_FP8) {
     ksc = a.k_scale[h];
     vsc = a.v_scale[h];
   }
-  const uint4 kx = *reinterpret_cast<const uint4*>(krow + size_t(min(lane, cpr - 1)) * 16);
-  uint32_t vx[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int d = min(lane + 64 * i, D - 1);
-    if constexpr (IN_ES == 4) vx[i] = *reinterpret_cast<const uint32_t*>(vrow + size_t(d) * 4);
-    else if constexpr (IN_ES == 2) vx[i] = *reinterpret_cast<const uint16_t*>(vrow + size_t(d) * 2);
-    else vx[i] = *reinterpret_cast<const uint8_t*>(vrow + d);
-  }
-  if (slot < 0) return;
-  const int blk = slot / BS, off = slot % BS;
-  char* kdst = static_cast<char*>(a.k_cache) + ((size_t(blk) * H + h) * BS + off) * size_t(D) * OUT_ES;
-  char* vdst = static_cast<char*>(a.v_cache) + (size_t(blk) * H + h) * size_t(D) * BS * OUT_ES + size_t(off) * OUT_ES;
-  if (lane < cpr) {
-    if constexpr (KV != KV_FP8) {
-      *reinterpret_cast<uint4*>(kdst + size_t(lane) * 16) = kx;
-    } else {
-      const uint32_t w[4] = {kx.x, kx.y, kx.z, kx.w};
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t c0 = e4m3_encode(bf16_lo(w[e]) / ksc);
-        const uint32_t c1 = e4m3_encode(bf16_hi(w[e]) / ksc);
-        const uint32_t two = c0 | (c1 << 8);
-        if (e < 2) lo |= two << (16 * e); else hi |= two << (16 * (e - 2));
-      }
-      *reinterpret_cast<uint2*>(kdst + size_t(lane) * 8) = make_uint2(lo, hi);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if (i >= vpl) break;
-    const int d = lane + 64 * i;
-    char* p = vdst + size_t(d) * BS * OUT_ES;
-    if constexpr (OUT_ES == 4) *reinterpret_cast<uint32_t*>(p) = vx[i];
-    else if constexpr (OUT_ES == 2) *reinterpret_cast<uint16_t*>(p) = uint16_t(vx[i]);
-    else if constexpr (KV == KV_FP8_RAW) *p = char(vx[i]);
-    else *p = char(e4m3_encode(bf16_lo(vx[i]) / vsc));
-  }
+  store_row<KV>(krow, vrow, a.k_cache, a.v_cache, a.slot_mapping[t], h, H, D, a.block_size, ksc, vsc);
 }
 
 // One workgroup row per pair; 16-byte chunks of the block in both pools.

@@ -114,6 +114,27 @@ def decode_step(g: GpuBatch, out=None, partition_tokens=64, workspace=None) -> t
                      partition_tokens=partition_tokens, workspace=workspace)
 
 
+def decode_step_append(g: GpuBatch, out=None, partition_tokens=64, workspace=None) -> torch.Tensor:
+    """The decode step's store and attention in one pa_decode_append call: a
+    batch of decodes only, one new token per sequence (the step rows, in
+    sequence order)."""
+    b = g.batch
+    new = np.asarray(b.new_lens)
+    if b.is_chunk.any() or np.any(new > 1) or np.any((new == 0) & (np.asarray(b.total_lens) > 0)):
+        raise ValueError("decode_step_append takes a batch of decodes with one new token each (or empty ones)")
+    d = g.dec
+    S, H, D = b.num_seqs, b.num_kv_heads, b.head_dim
+    k_new, v_new = g.k_step.view(-1, H, D), g.v_step.view(-1, H, D)
+    if np.any(new == 0):                               # empty sequences: rows that nothing stores
+        idx = torch.from_numpy(np.flatnonzero(new == 1)).to(k_new.device)
+        k_full = torch.zeros((S, H, D), dtype=k_new.dtype, device=k_new.device)
+        v_full = torch.zeros_like(k_full)
+        k_full[idx], v_full[idx] = k_new, v_new
+        k_new, v_new = k_full, v_full
+    return pa.decode_append(g.cache, k_new, v_new, d["q"], d["table"], d["lens"], d["max_len"], b.scale, out=out,
+                            partition_tokens=partition_tokens, workspace=workspace)
+
+
 def pack_args(g: GpuBatch, device="cuda") -> dict:
     """Device arguments of pa_pack_kv for every sequence's tokens (cached and
     stepped), in order."""

@@ -88,6 +88,38 @@ def test_decode_with_no_sequences_is_a_noop():
     assert decode_call(cache(), S=0) == L.PA_OK
 
 
+def append_call(c, k_new=FAKE, v_new=FAKE, **kw):
+    a = dict(q=FAKE, q_dtype=L.PA_BF16, out=FAKE, out_dtype=L.PA_BF16, S=2, Hq=4, scale=0.125, table=FAKE,
+             max_blocks=4, lens=FAKE, max_ctx=64, part=0, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return L.lib().pa_decode_append(C.byref(c) if c is not None else None, k_new, v_new, a["q"], a["q_dtype"],
+                                    a["out"], a["out_dtype"], a["S"], a["Hq"], a["scale"], a["table"],
+                                    a["max_blocks"], a["lens"], a["max_ctx"], a["part"], a["ws"], a["ws_bytes"],
+                                    None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k_new=None), L.PA_ERR_NULL),
+    (dict(v_new=None), L.PA_ERR_NULL),
+    (dict(c=None), L.PA_ERR_NULL),
+    (dict(c=cache(head_dim=96)), L.PA_ERR_UNSUPPORTED),
+    (dict(Hq=3), L.PA_ERR_SHAPE),
+    (dict(part=100), L.PA_ERR_SHAPE),
+    (dict(ws_bytes=16), L.PA_ERR_WORKSPACE),
+])
+def test_decode_append_rejects_bad_arguments(kw, code):
+    c = kw.pop("c", cache())
+    assert append_call(c, **kw) == code
+    err = L.lib().pa_last_error()
+    assert err
+    if kw.keys() & {"k_new", "v_new"}:
+        assert b"pa_decode_append" in err
+
+
+def test_decode_append_with_no_sequences_is_a_noop():
+    assert append_call(cache(), S=0, k_new=None, v_new=None) == L.PA_OK
+
+
 def test_store_and_copy_reject_bad_arguments():
     lib = L.lib()
     c = cache()

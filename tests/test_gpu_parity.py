@@ -323,6 +323,56 @@ def test_every_compiled_decode_shape(kv, d, B, G):
     assert np.array_equal(bits(k, kv), oracle_bits(kr, kv)) and np.array_equal(bits(v, kv), oracle_bits(vr, kv))
 
 
+def _append_vs_store_then_decode(batch, partitions=(64,)):
+    """pa_decode_append against pa_store_kv followed by pa_decode on a second
+    copy of the same cache: outputs and both pools bit for bit."""
+    from paged_kv_attention_26_amd import runner
+    for part in partitions:
+        ga, gb = runner.prepare(batch), runner.prepare(batch)
+        runner.store_step(ga)
+        want = runner.decode_step(ga, partition_tokens=part)
+        got = runner.decode_step_append(gb, partition_tokens=part)
+        torch.cuda.synchronize()
+        raw = lambda t: t.contiguous().view(torch.uint8)  # bytes: the pools' poison pattern is a NaN
+        assert torch.equal(raw(want), raw(got))
+        assert torch.equal(raw(ga.cache.k_cache), raw(gb.cache.k_cache))
+        assert torch.equal(raw(ga.cache.v_cache), raw(gb.cache.v_cache))
+        del ga, gb
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("B", [16, 32])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_append_every_compiled_shape(kv, d, B, G):
+    """The store-and-decode launch (pa_decode_append) in every (cache dtype,
+    head_dim, block size, group) the decode compiles, on a ragged batch with
+    empty and one-token sequences, at 64-token partitions and without a
+    split: the same outputs and pools, bit for bit, as the store followed by
+    the decode."""
+    rng = np.random.default_rng(900 + 97 * G + B + d)
+    lens = np.concatenate([[0, 1, B - 1, B, B + 1, 200], rng.integers(1, 300, 4)])
+    prior = np.maximum(lens - 1, 0)
+    new = (lens > 0).astype(np.int64)
+    io = "f32" if kv == "f32" else "bf16"
+    batch = W.paged_batch(f"append-{kv}-d{d}-b{B}-g{G}", 900 + G, kv_dtype=kv, io_dtype=io, Hq=2 * G, Hkv=2, d=d,
+                          B=B, prior_lens=prior, new_lens=new, is_chunk=np.zeros(len(lens), bool), rng=rng)
+    say(f"[gpu] decode append {batch.name}")
+    _append_vs_store_then_decode(batch, partitions=(64, 0))
+
+
+@pytest.mark.parametrize("name", ["edge-fp8-b32", "skew", "many", "qwen3-8b-layer"])
+def test_decode_append_larger_batches(name):
+    """pa_decode_append on the edge lengths (fp8, block 32, partitions of 64,
+    512 and none), one long sequence among empty ones, 600 sequences (the
+    LDS prefix) and the full Qwen3-8B layer as benchmarked: bit for bit the
+    store followed by the decode."""
+    batch = {"edge-fp8-b32": lambda: edge_batch("fp8", 32), "skew": skew_batch, "many": many_batch,
+             "qwen3-8b-layer": W.config2}[name]()
+    say(f"[gpu] decode append {name}")
+    _append_vs_store_then_decode(batch, partitions=(64, 512, 0) if name.startswith("edge") else (64,))
+
+
 def test_step_replays_in_a_hip_graph():
     """A decode step (store of the step's tokens, then pa_decode with a
     caller-owned workspace) captured in a HIP graph: no call allocates or
