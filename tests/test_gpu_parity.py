@@ -373,19 +373,24 @@ def test_decode_append_larger_batches(name):
     _append_vs_store_then_decode(batch, partitions=(64, 512, 0) if name.startswith("edge") else (64,))
 
 
-def test_step_replays_in_a_hip_graph():
-    """A decode step (store of the step's tokens, then pa_decode with a
-    caller-owned workspace) captured in a HIP graph: no call allocates or
-    synchronises, so it captures, and every replay, with eager work and
-    synchronisation between replays, gives the eager result bit for bit."""
+@pytest.mark.parametrize("form", ["separate", "fused"])
+def test_step_replays_in_a_hip_graph(form):
+    """A decode step with a caller-owned workspace captured in a HIP graph,
+    in both forms: the store of the step's tokens then pa_decode, or one
+    pa_decode_append.  No call allocates or synchronises, so it captures,
+    and every replay, with eager work and synchronisation between replays,
+    gives the eager result bit for bit."""
     from paged_kv_attention_26_amd import binding as pa, runner
-    say("[gpu] decode step in a HIP graph")
+    say(f"[gpu] decode step in a HIP graph ({form})")
     batch = W.config2(small=True)
     g = runner.prepare(batch)
     ws = pa.decode_workspace(1, 1, batch.head_dim, 1, 0)
     out = torch.empty_like(g.dec["q"])
 
     def step():
+        if form == "fused":
+            runner.decode_step_append(g, out=out, workspace=ws)
+            return
         runner.store_step(g)
         runner.decode_step(g, out=out, workspace=ws)
     step()
