@@ -364,13 +364,14 @@ def test_decode_append_every_compiled_shape(kv, d, B, G):
 @pytest.mark.parametrize("name", ["edge-fp8-b32", "skew", "many", "qwen3-8b-layer"])
 def test_decode_append_larger_batches(name):
     """pa_decode_append on the edge lengths (fp8, block 32, partitions of 64,
-    512 and none), one long sequence among empty ones, 600 sequences (the
-    LDS prefix) and the full Qwen3-8B layer as benchmarked: bit for bit the
-    store followed by the decode."""
+    512 and none), one long sequence among empty ones (64 and none), 600
+    sequences (the LDS prefix; 64, 256 and none) and the full Qwen3-8B layer
+    as benchmarked: bit for bit the store followed by the decode."""
     batch = {"edge-fp8-b32": lambda: edge_batch("fp8", 32), "skew": skew_batch, "many": many_batch,
              "qwen3-8b-layer": W.config2}[name]()
     say(f"[gpu] decode append {name}")
-    _append_vs_store_then_decode(batch, partitions=(64, 512, 0) if name.startswith("edge") else (64,))
+    parts = {"edge-fp8-b32": (64, 512, 0), "skew": (64, 0), "many": (64, 256, 0), "qwen3-8b-layer": (64,)}[name]
+    _append_vs_store_then_decode(batch, partitions=parts)
 
 
 @pytest.mark.parametrize("form", ["separate", "fused"])
@@ -1146,6 +1147,7 @@ def test_decode_random_shapes(seed):
     err = np.max(np.abs(out - ref)) if out.size else 0.0
     say(f"      max abs err {err:.3e}")
     assert err < TOL[batch.kv_dtype]
+    _append_vs_store_then_decode(batch, partitions=(part,))   # the store inside the launch: bit for bit
 
 
 def random_chunk_batch(seed):
