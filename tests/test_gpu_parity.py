@@ -361,16 +361,18 @@ def test_decode_append_every_compiled_shape(kv, d, B, G):
     _append_vs_store_then_decode(batch, partitions=(64, 0))
 
 
-@pytest.mark.parametrize("name", ["edge-fp8-b32", "skew", "many", "qwen3-8b-layer"])
+@pytest.mark.parametrize("name", ["edge-fp8-b32", "skew", "many", "max-seqs", "qwen3-8b-layer"])
 def test_decode_append_larger_batches(name):
     """pa_decode_append on the edge lengths (fp8, block 32, partitions of 64,
     512 and none), one long sequence among empty ones (64 and none), 600
-    sequences (the LDS prefix; 64, 256 and none) and the full Qwen3-8B layer
-    as benchmarked: bit for bit the store followed by the decode."""
+    sequences (the LDS prefix; 64, 256 and none), 8192 sequences of 0 to 40
+    tokens (the most one call takes; 16 and none) and the full Qwen3-8B
+    layer as benchmarked: bit for bit the store followed by the decode."""
     batch = {"edge-fp8-b32": lambda: edge_batch("fp8", 32), "skew": skew_batch, "many": many_batch,
-             "qwen3-8b-layer": W.config2}[name]()
+             "max-seqs": max_seqs_batch, "qwen3-8b-layer": W.config2}[name]()
     say(f"[gpu] decode append {name}")
-    parts = {"edge-fp8-b32": (64, 512, 0), "skew": (64, 0), "many": (64, 256, 0), "qwen3-8b-layer": (64,)}[name]
+    parts = {"edge-fp8-b32": (64, 512, 0), "skew": (64, 0), "many": (64, 256, 0), "max-seqs": (16, 0),
+             "qwen3-8b-layer": (64,)}[name]
     _append_vs_store_then_decode(batch, partitions=parts)
 
 
