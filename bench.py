@@ -34,8 +34,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0       # published dense bf16 matrix peak
 # and WRITE_SIZE passes scaled by the same counters on a plain 1 GiB copy
 # (bench.py --copy-probe 1024), and the hash of the kernel sources they were
 # taken on: once those sources change the figure no longer applies.
-DECODE_TRAFFIC = {"sources_sha256": "7297795b754726b56dfe567c0d711b70b90a3e79e05573a955dd0a97ea559105",
-                  "bytes_per_launch": 307067887}
+DECODE_TRAFFIC = {"sources_sha256": "7a6cfb9a9c8ffe173c27e6db2e6d68aeed638fa89e1d733295b7f798ae77942d",
+                  "bytes_per_launch": 305882633}
 DECODE_SOURCES = ("decode_kernel.h", "store_row.h", "pa_device.h", "pa_internal.h", "decode_bf16.hip")
 
 
@@ -133,30 +133,34 @@ def hbm_probe(torch):
     """Practical HBM ceilings on this GPU from the reference kernels of
     libpa_probe.so: a streaming read of 4 GiB, a copy of 2 GiB (read + write
     counted), and whole 4 KB tiles of a 4 GiB buffer read once each in a
-    seeded random order (decode's access pattern).  Median of 20 calls, each
-    after a cache flush."""
+    seeded random order (decode's access pattern), each with the default
+    cache policy and with the non-temporal hint on the loads ("_nt").
+    Median of 20 calls, each after a cache flush."""
     import ctypes as C
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_attention_26_amd", "libpa_probe.so")
     lib = C.CDLL(path)
-    lib.pa_probe_read.argtypes = [C.c_void_p, C.c_size_t, C.c_int, C.c_void_p, C.c_void_p]
-    lib.pa_probe_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_void_p]
-    lib.pa_probe_tiles.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int, C.c_void_p, C.c_void_p]
+    lib.pa_probe_read.argtypes = [C.c_void_p, C.c_size_t, C.c_int, C.c_void_p, C.c_int, C.c_void_p]
+    lib.pa_probe_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_int, C.c_void_p]
+    lib.pa_probe_tiles.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int, C.c_void_p, C.c_int, C.c_void_p]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     grid = cus * 8
     stream = lambda: C.c_void_p(torch.cuda.current_stream().cuda_stream)
     big = torch.zeros(1 << 32, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(grid * 256, dtype=torch.int32, device="cuda")
-    out = {}
-    med, _, _ = timed_calls(lambda: lib.pa_probe_read(big.data_ptr(), big.numel(), grid, sink.data_ptr(), stream()), 20)
-    out["stream_read_4GiB"] = dict(GBps=round(big.numel() / med / 1e6, 1), ms=round(med, 4))
     half = big.numel() // 2
-    med, _, _ = timed_calls(lambda: lib.pa_probe_copy(big.data_ptr(), big.data_ptr() + half, half, grid, stream()), 20)
-    out["copy_2GiB_read_plus_write"] = dict(GBps=round(2 * half / med / 1e6, 1), ms=round(med, 4))
     n_tiles = big.numel() // 4096
     order = torch.from_numpy(np.random.default_rng(11).permutation(n_tiles).astype(np.int32)).cuda()
-    med, _, _ = timed_calls(lambda: lib.pa_probe_tiles(big.data_ptr(), order.data_ptr(), n_tiles, cus * 4,
-                                                       sink.data_ptr(), stream()), 20)
-    out["random_4KB_tiles_read_4GiB"] = dict(GBps=round(big.numel() / med / 1e6, 1), ms=round(med, 4))
+    out = {}
+    for nt, sfx in ((0, ""), (1, "_nt")):
+        med, _, _ = timed_calls(lambda: lib.pa_probe_read(big.data_ptr(), big.numel(), grid, sink.data_ptr(), nt,
+                                                          stream()), 20)
+        out["stream_read_4GiB" + sfx] = dict(GBps=round(big.numel() / med / 1e6, 1), ms=round(med, 4))
+        med, _, _ = timed_calls(lambda: lib.pa_probe_copy(big.data_ptr(), big.data_ptr() + half, half, grid, nt,
+                                                          stream()), 20)
+        out["copy_2GiB_read_plus_write" + sfx] = dict(GBps=round(2 * half / med / 1e6, 1), ms=round(med, 4))
+        med, _, _ = timed_calls(lambda: lib.pa_probe_tiles(big.data_ptr(), order.data_ptr(), n_tiles, cus * 4,
+                                                           sink.data_ptr(), nt, stream()), 20)
+        out["random_4KB_tiles_read_4GiB" + sfx] = dict(GBps=round(big.numel() / med / 1e6, 1), ms=round(med, 4))
     del big, sink, order
     torch.cuda.empty_cache()
     return out
