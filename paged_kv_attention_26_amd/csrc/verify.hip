@@ -78,6 +78,21 @@ __device__ __forceinline__ void vstore2(float* p, float x, float y) {
   const uint64_t b = uint64_t(__float_as_uint(x)) | (uint64_t(__float_as_uint(y)) << 32);
   __hip_atomic_store(reinterpret_cast<uint64_t*>(p), b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// V operand loads with the non-temporal hint (nt): each of them reads 32
+// rows x 32 contiguous bytes of a transposed V tile, whole lines, and no
+// line is read twice in the launch (5.2% faster on the Qwen3-8B verify
+// batch, 9.5% on the long-context prefixes).  The K operand loads keep the
+// default policy: each reads 32 bytes of every 256-byte key row, so the four
+// loads of one line would each fetch it again (with the hint on both, 28%
+// slower).
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 stream_load(const uint2* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
 __device__ __forceinline__ void vload2(const float* p, float& x, float& y) {
   const uint64_t b = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
@@ -331,7 +346,7 @@ __global__ void __launch_bounds__(kVerifyThreads) verify_kernel(PrefillArgs a,
       const char* vb = vpool + (size_t(bid) * Hkv + s.kvh) * size_t(D * B * ES) + (kb % B) * ES;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        va[dt][ks] = *reinterpret_cast<const typename Raw::T*>(vb + size_t(32 * dt + n) * (B * ES));
+        va[dt][ks] = stream_load(reinterpret_cast<const typename Raw::T*>(vb + size_t(32 * dt + n) * (B * ES)));
     }
   };
 
