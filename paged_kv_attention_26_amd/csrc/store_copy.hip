@@ -16,6 +16,19 @@
 
 namespace pa {
 
+// 16-byte loads with the non-temporal hint (nt), for data a launch reads
+// once with each line read whole by one instruction: the block copy's
+// source blocks (5.39 -> 6.02 TB/s) and the tile store's key input rows
+// (16 lanes take a head's 256-byte slice of a token row; 4.95 -> 5.03 TB/s).
+// The store's value input loads take one 16-byte chunk of a token row per
+// lane, eight instructions to a line, and keep the default policy: with the
+// hint on them too the store lost a third of its bandwidth.  Stores keep the
+// default policy (with the hint both kernels measured slower).
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // One workgroup = 64 consecutive tokens x one kv head.
 //  K: 16-byte input chunks, mapped so that consecutive lanes cover one key
 //     row: reads and writes are both contiguous.
@@ -74,7 +87,7 @@ __global__ void __launch_bounds__(256) store_kv_kernel(StoreArgs a) {
 #pragma unroll
   for (int i = 0; i < KI; ++i) {
     const int idx = min(int(threadIdx.x) + 256 * i, nkc - 1);
-    kx[i] = *reinterpret_cast<const uint4*>(kin + ((size_t(t0 + idx / cpr) * H + h) * D + size_t(idx % cpr) * EPC) * IN_ES);
+    kx[i] = stream_load(reinterpret_cast<const uint4*>(kin + ((size_t(t0 + idx / cpr) * H + h) * D + size_t(idx % cpr) * EPC) * IN_ES));
     ks[i] = a.slot_mapping[t0 + idx / cpr];
   }
   // values: lane = token, wave w takes chunks w, w + 4, ...
@@ -245,21 +258,8 @@ __global__ void __launch_bounds__(256) store_rows_kernel(StoreArgs a) {
   store_row<KV>(krow, vrow, a.k_cache, a.v_cache, a.slot_mapping[t], h, H, D, a.block_size, ksc, vsc);
 }
 
-// 16-byte loads and stores with the non-temporal hint (nt): the copy reads
-// each source line once, whole, in one instruction, and nothing in the launch
-// reads it again.  (Where several instructions or workgroups read parts of
-// one line -- the store's per-head input rows, the verification kernel's
-// operand rows -- the hint costs a third of the bandwidth, and it is not used.)
-__device__ __forceinline__ uint4 stream_load(const uint4* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ void stream_store(uint4* p, const uint4& x) {
-  __builtin_nontemporal_store(u32x4_t{x.x, x.y, x.z, x.w}, reinterpret_cast<u32x4_t*>(p));
-}
-
 // One workgroup row per pair; 16-byte chunks of the block in both pools,
-// loaded with the non-temporal hint (5.39 -> 6.02 TB/s on 11 164 pairs).
+// loaded with the non-temporal hint.
 __global__ void __launch_bounds__(256) copy_blocks_kernel(CopyArgs a) {
   const int p = blockIdx.x;
   const int src = a.pairs[2 * p], dst = a.pairs[2 * p + 1];
